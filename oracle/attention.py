@@ -1,0 +1,177 @@
+"""Plain two-pass exact attention in float64 (the oracle).  TEST INFRASTRUCTURE.
+
+Definition followed: Attention(Q, K, V) = softmax(Q K^T * scale) V, row-wise
+softmax over keys ("From standard Attention to FlashAttention and paged
+execution", dlog.com.cn, section "the memory bottleneck of standard attention";
+the 1/sqrt(d) scale is the one in that section's code, passed explicitly here
+because the page's worked example of section 2.1 omits it).  The per-row
+logsumexp is the statistic the tiled forward writes next to O ("L2.5 SOTA
+Kernel", yulong.wang, sections 2.1 and 2.3).
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* causal mask: key j is admissible for query row i iff j <= i + (Lk - Lq)
+  (bottom-right alignment; j <= i when Lq == Lk);
+* a row with no admissible key has O = 0 and lse = -inf;
+* lse = m + ln(l), natural log, in units of the scaled score;
+* keys past a sequence's end simply do not exist (never a zero-filled key).
+
+Rows are independent (dlog.com.cn, section 2.1), so computing a chunk of rows at
+a time is exact; it only bounds memory.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns (uint16) to float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _as_f64(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_rows(q, k, v, scale: float, causal: bool = False, row_chunk: int = 512,
+                   rows=None):
+    """Exact attention for one head.
+
+    q [Lq, d], k [Lk, d], v [Lk, dv] (float arrays or bf16 bits).  Returns
+    (O [n, dv] float64, lse [n] float64) for query rows ``rows`` (default all).
+
+    Pass 1: m_i = max_j s_ij.  Pass 2: P_ij = exp(s_ij - m_i), l_i = sum_j P_ij,
+    O_i = sum_j P_ij v_j / l_i, lse_i = m_i + ln l_i.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    rows = np.arange(lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    lse = np.full(len(rows), NEG_INF, dtype=np.float64)
+    if lk == 0 or len(rows) == 0:
+        return o, lse
+    for a in range(0, len(rows), row_chunk):
+        r = rows[a:a + row_chunk]
+        # under a causal mask no row of this chunk sees keys past the last row's limit
+        kmax = lk if not causal else int(min(lk, max(0, r.max() + (lk - lq) + 1)))
+        if kmax <= 0:
+            continue
+        s = (q[r] @ k[:kmax].T) * scale
+        if causal:
+            # admissible iff j <= i + (Lk - Lq)
+            s = np.where(np.arange(kmax)[None, :] <= (r[:, None] + (lk - lq)), s, NEG_INF)
+        m = s.max(axis=1)                                  # pass 1
+        has = np.isfinite(m)
+        m_safe = np.where(has, m, 0.0)
+        p = np.exp(s - m_safe[:, None])                    # pass 2 (exp(-inf) = 0)
+        l = p.sum(axis=1)
+        pv = p @ v[:kmax]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o[a:a + len(r)] = np.where(has[:, None], pv / np.where(has, l, 1.0)[:, None], 0.0)
+            lse[a:a + len(r)] = np.where(has, m_safe + np.log(np.where(has, l, 1.0)), NEG_INF)
+    return o, lse
+
+
+def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
+    """Debug hook for tiny inputs: the full softmax matrix P [Lq, Lk] (two-pass)."""
+    q, k = _as_f64(q), _as_f64(k)
+    lq, lk = q.shape[0], k.shape[0]
+    s = (q @ k.T) * scale
+    if causal:
+        s = np.where(np.arange(lk)[None, :] <= (np.arange(lq)[:, None] + (lk - lq)), s, NEG_INF)
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.where(l > 0, p / np.where(l > 0, l, 1.0), 0.0)
+
+
+def attention_dense(q, k, v, scale: float, causal: bool = False, heads=None, rows=None):
+    """Dense batched attention, Q [B, H, N, d], K/V [B, H, Nk, d] (the [B, H, N, d]
+    layout of the pages' Triton kernels).  Returns O [B, H, N, d] and lse [B, H, N]
+    float64.  ``heads`` restricts to a list of (b, h) pairs (the other entries stay
+    NaN); ``rows`` restricts the query rows (same for each head)."""
+    B, H, N, d = q.shape
+    dv = v.shape[3]
+    o = np.full((B, H, N, dv), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        ob, lb = attention_rows(q[b, h], k[b, h], v[b, h], scale, causal, rows=rows)
+        if rows is None:
+            o[b, h], lse[b, h] = ob, lb
+        else:
+            o[b, h, rows], lse[b, h, rows] = ob, lb
+    return o, lse
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, seqs=None,
+                     heads=None, rows_per_seq=None):
+    """Variable-length packed attention ("From standard Attention to FlashAttention
+    and paged execution", section 3.3): tokens of all sequences are flattened to
+    Q [total_q, H, d] and K/V [total_k, H, d]; sequence s owns rows
+    [cu_q[s], cu_q[s+1]) of Q and [cu_k[s], cu_k[s+1]) of K/V (the page's example
+    cu_seqlens [0, 3, 7] means ranges [0,3) and [3,7)).  Each sequence is attended
+    independently.  Returns O [total_q, H, d], lse [total_q, H] (NaN where not
+    computed when restricted by ``seqs``/``heads``/``rows_per_seq``)."""
+    tq, H, d = q.shape
+    dv = v.shape[2]
+    o = np.full((tq, H, dv), np.nan)
+    lse = np.full((tq, H), np.nan)
+    S = len(cu_q) - 1
+    seqs = range(S) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for s in seqs:
+        q0, q1 = int(cu_q[s]), int(cu_q[s + 1])
+        k0, k1 = int(cu_k[s]), int(cu_k[s + 1])
+        rows = None
+        if rows_per_seq is not None:
+            rows = np.asarray(rows_per_seq(s, q1 - q0), dtype=np.int64)
+        for h in heads:
+            ob, lb = attention_rows(q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], scale, causal,
+                                    rows=rows)
+            if rows is None:
+                o[q0:q1, h], lse[q0:q1, h] = ob, lb
+            else:
+                o[q0 + rows, h], lse[q0 + rows, h] = ob, lb
+    return o, lse
+
+
+def gather_paged(cache, block_table_row, ctx: int, page: int):
+    """Contiguous [ctx, H, d] view of one sequence's cached keys (or values): token t
+    lives in physical page block_table[t // page], slot t % page ("From standard
+    Attention to FlashAttention and paged execution", sections "PagedAttention" and
+    "the two functions v3 calls")."""
+    n = (ctx + page - 1) // page
+    pages = np.asarray(block_table_row[:n], dtype=np.int64)
+    g = cache[pages]  # [n, page, H, d]
+    return g.reshape(n * page, *cache.shape[2:])[:ctx]
+
+
+def attention_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale: float,
+                           seqs=None, heads=None):
+    """Decode over a paged KV cache: sequence b's single query q[b] [H, d] attends
+    its context_lens[b] cached tokens, gathered through block_table[b] (page size =
+    k_cache.shape[1]).  With one query token, bottom-right causal and non-causal
+    coincide.  Returns O [B, H, d], lse [B, H] (NaN where not computed)."""
+    B, H, d = q.shape
+    page = k_cache.shape[1]
+    dv = v_cache.shape[3]
+    o = np.full((B, H, dv), np.nan)
+    lse = np.full((B, H), np.nan)
+    seqs = range(B) if seqs is None else seqs
+    heads = list(range(H)) if heads is None else list(heads)
+    for b in seqs:
+        ctx = int(context_lens[b])
+        kb = gather_paged(k_cache, block_table[b], ctx, page)
+        vb = gather_paged(v_cache, block_table[b], ctx, page)
+        for h in heads:
+            ob, lb = attention_rows(q[b, h][None, :], kb[:, h], vb[:, h], scale, False)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse

@@ -1,0 +1,361 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  None of them re-types the oracle's formula:
+each compares it with a printed value, a closed form, an invariant, a brute-force
+loop or a second algorithm (the online recurrence).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.golden.load import load
+
+TIGHT = 1e-12
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- worked example (page 1, §2.1)
+
+def test_hand_example_closed_form():
+    g = load("hand_example.txt")
+    Q, K, V = g["Q"], g["K"], g["V"]
+    # scores are integers: S = Q K^T exactly as printed
+    P = oracle.probabilities(Q, K, 1.0)
+    e3, e2 = math.exp(3), math.exp(2)
+    P_exact = np.array([[1 / (1 + e3), e3 / (1 + e3)], [1 / (1 + e2), e2 / (1 + e2)]])
+    assert np.abs(P - P_exact).max() < TIGHT
+    O, lse = oracle.attention_rows(Q, K, V, 1.0)
+    O_exact = P_exact @ V
+    assert np.abs(O - O_exact).max() < TIGHT
+    assert abs(O_exact[0, 1] - 1.9051483) < 1e-7
+    lse_exact = np.array([5 + math.log1p(math.exp(-3)), 3 + math.log1p(math.exp(-2))])
+    assert np.abs(lse - lse_exact).max() < TIGHT
+    # third column of V is all ones -> third column of O is exactly a row sum of P
+    assert np.abs(O[:, 2] - 1.0).max() < 1e-15
+
+
+def test_hand_example_printed_values():
+    """Printed P (2 dp) and O (2 dp).  The page multiplied its rounded P, so O[0,1] is
+    printed 1.90 while the exact value is 1.905; hence the ±0.01 bound on O."""
+    g = load("hand_example.txt")
+    S = g["Q"] @ g["K"].T
+    assert np.array_equal(S, g["S"])
+    P = oracle.probabilities(g["Q"], g["K"], 1.0)
+    assert np.abs(P - g["P"]).max() <= 0.005 + 1e-12
+    O, _ = oracle.attention_rows(g["Q"], g["K"], g["V"], 1.0)
+    assert np.abs(O - g["O"]).max() <= 0.01
+
+
+def test_hand_example_transposed_operand_is_caught():
+    """A swapped Q/K (S^T instead of S) would give a different O on this example."""
+    g = load("hand_example.txt")
+    O, _ = oracle.attention_rows(g["Q"], g["K"], g["V"], 1.0)
+    Ot, _ = oracle.attention_rows(g["K"], g["Q"], g["V"], 1.0)
+    assert np.abs(O - Ot).max() > 0.1
+
+
+# ----------------------------------------------------------------- FA2 trace (page 1, §2.3)
+
+def _fa2_inputs():
+    g = load("fa2_trace.txt")
+    Q = np.stack([g["s0"], g["s1"]])      # with K = I, S = Q K^T = Q: scores as printed
+    K = np.eye(4)
+    return g, Q, K, g["Vread"]
+
+
+def test_fa2_trace_online_recurrence():
+    g, Q, K, V = _fa2_inputs()
+    O, lse, tr = oracle.online_attention(Q, K, V, 1.0, block=1, trace=True)
+    for r, key in ((0, "ml0"), (1, "ml1")):
+        assert np.abs(np.array(tr[r]) - g[key]).max() < 5e-5
+    assert np.abs(O[0] - g["O0"]).max() < 5e-5
+    assert np.abs(O[1] - g["O1"]).max() < 5e-5
+    l0 = 1 + math.exp(-1) + math.exp(-2) + math.exp(-3)
+    l1 = 1 + math.exp(-2) + math.exp(-3) + math.exp(-4)
+    assert abs(tr[0][-1][1] - l0) < TIGHT and abs(tr[1][-1][1] - l1) < TIGHT
+    assert abs(lse[0] - (3 + math.log(l0))) < TIGHT and abs(lse[1] - (4 + math.log(l1))) < TIGHT
+
+
+def test_fa2_trace_two_pass():
+    g, Q, K, V = _fa2_inputs()
+    O, lse = oracle.attention_rows(Q, K, V, 1.0)
+    assert np.abs(O[0] - g["O0"]).max() < 5e-5
+    assert np.abs(O[1] - g["O1"]).max() < 5e-5
+    assert abs(lse[0] - 3.4401897) < 1e-7 and abs(lse[1] - 4.1851825) < 1e-7
+
+
+# ----------------------------------------------------------------- invariants and closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_of_p_sum_to_one_and_output_is_convex(causal):
+    r = rng(1)
+    q, k, v = r.normal(size=(9, 5)), r.normal(size=(9, 5)), r.normal(size=(9, 3))
+    P = oracle.probabilities(q, k, 0.7, causal)
+    assert np.abs(P.sum(1) - 1).max() < 1e-14
+    assert (P >= 0).all()
+    if causal:
+        assert np.all(P[np.triu_indices(9, 1)] == 0)
+    O, _ = oracle.attention_rows(q, k, v, 0.7, causal)
+    assert (O >= v.min(0) - 1e-15).all() and (O <= v.max(0) + 1e-15).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lq,lk", [(7, 7), (5, 9), (1, 6), (13, 13)])
+@pytest.mark.parametrize("block", [1, 2, 3, 7, None])
+def test_online_recurrence_equals_two_pass(causal, lq, lk, block):
+    r = rng(lq * 100 + lk)
+    q, k, v = r.normal(size=(lq, 6)), r.normal(size=(lk, 6)), r.normal(size=(lk, 4))
+    o1, l1 = oracle.online_attention(q, k, v, 0.45, block=block or lk, causal=causal)
+    o2, l2 = oracle.attention_rows(q, k, v, 0.45, causal)
+    assert np.abs(o1 - o2).max() < TIGHT
+    assert np.abs(l1 - l2).max() < TIGHT
+
+
+def _brute(q, k, v, scale, causal):
+    """Pure-Python attention with math.exp, no NumPy arithmetic and no max-subtraction
+    (inputs are small enough for exp not to overflow)."""
+    lq, lk, d, dv = len(q), len(k), len(q[0]), len(v[0])
+    O, L = [], []
+    for i in range(lq):
+        w = []
+        for j in range(lk):
+            if causal and j > i + (lk - lq):
+                continue
+            s = 0.0
+            for c in range(d):
+                s += float(q[i][c]) * float(k[j][c])
+            w.append((j, math.exp(scale * s)))
+        z = sum(x for _, x in w)
+        O.append([sum(x * float(v[j][c]) for j, x in w) / z if w else 0.0 for c in range(dv)])
+        L.append(math.log(z) if w else -math.inf)
+    return np.array(O), np.array(L)
+
+
+@pytest.mark.parametrize("lq,lk,d,causal", [(1, 1, 1, False), (1, 5, 3, False), (4, 4, 8, True),
+                                            (16, 16, 8, False), (16, 16, 8, True), (3, 11, 2, True),
+                                            (11, 3, 5, False), (7, 13, 4, True)])
+def test_brute_force_small(lq, lk, d, causal):
+    r = rng(lq + 7 * lk + 31 * d)
+    q, k, v = r.normal(size=(lq, d)), r.normal(size=(lk, d)), r.normal(size=(lk, 3))
+    scale = 1 / math.sqrt(d)
+    ob, lb = _brute(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    o, l = oracle.attention_rows(q, k, v, scale, causal)
+    assert np.array_equal(np.isinf(l), np.isinf(lb))
+    fin = np.isfinite(lb)
+    assert np.abs(o - ob).max() < TIGHT
+    assert np.abs(l[fin] - lb[fin]).max() < TIGHT
+
+
+def test_causal_invariants():
+    r = rng(3)
+    n, d = 12, 6
+    q, k, v = r.normal(size=(n, d)), r.normal(size=(n, d)), r.normal(size=(n, d))
+    s = 0.4
+    o, l = oracle.attention_rows(q, k, v, s, True)
+    # row 0 sees only key 0
+    assert np.abs(o[0] - v[0]).max() < 1e-15
+    assert abs(l[0] - s * (q[0] @ k[0])) < TIGHT
+    # last causal row == last non-causal row
+    o2, l2 = oracle.attention_rows(q, k, v, s, False)
+    assert np.abs(o[-1] - o2[-1]).max() < TIGHT and abs(l[-1] - l2[-1]) < TIGHT
+    # changing keys/values after row i leaves row i unchanged
+    i = 5
+    k2, v2 = k.copy(), v.copy()
+    k2[i + 1:] = r.normal(size=k2[i + 1:].shape) * 10
+    v2[i + 1:] = r.normal(size=v2[i + 1:].shape) * 10
+    o3, l3 = oracle.attention_rows(q, k2, v2, s, True)
+    assert np.abs(o3[:i + 1] - o[:i + 1]).max() == 0 and np.abs(l3[:i + 1] - l[:i + 1]).max() == 0
+    assert np.abs(o3[i + 1:] - o[i + 1:]).max() > 1e-3
+    # a single query row with causal (bottom-right) == non-causal
+    oa, la = oracle.attention_rows(q[:1], k, v, s, True)
+    ob, lb = oracle.attention_rows(q[:1], k, v, s, False)
+    assert np.abs(oa - ob).max() == 0 and np.abs(la - lb).max() == 0
+    # Lq < Lk: row i (bottom-right aligned) sees keys 0..i+(Lk-Lq)
+    oc, lc = oracle.attention_rows(q[:4], k, v, s, True)
+    for i in range(4):
+        lim = i + (n - 4)
+        od, ld = oracle.attention_rows(q[i:i + 1], k[:lim + 1], v[:lim + 1], s, False)
+        assert np.abs(oc[i] - od[0]).max() < TIGHT and abs(lc[i] - ld[0]) < TIGHT
+
+
+def test_rows_without_keys():
+    r = rng(4)
+    q, k, v = r.normal(size=(6, 4)), r.normal(size=(3, 4)), r.normal(size=(3, 4))
+    # Lq > Lk under bottom-right causal: rows 0..2 have no admissible key
+    o, l = oracle.attention_rows(q, k, v, 0.5, True)
+    assert np.all(o[:3] == 0) and np.all(np.isneginf(l[:3]))
+    assert np.all(np.isfinite(l[3:]))
+    # no keys at all
+    o, l = oracle.attention_rows(q, k[:0], v[:0], 0.5, False)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_closed_forms():
+    r = rng(5)
+    q, v = r.normal(size=(5, 4)), r.normal(size=(9, 3))
+    # zero keys -> uniform attention: O = mean(V), lse = ln(Lk)
+    o, l = oracle.attention_rows(q, np.zeros((9, 4)), v, 0.3)
+    assert np.abs(o - v.mean(0)).max() < TIGHT and np.abs(l - math.log(9)).max() < TIGHT
+    # one key -> O = v0, lse = scale q.k
+    k1 = r.normal(size=(1, 4))
+    o, l = oracle.attention_rows(q, k1, v[:1], 0.3)
+    assert np.abs(o - v[0]).max() < 1e-15 and np.abs(l - 0.3 * (q @ k1[0])).max() < TIGHT
+    # two keys: O = sigma(a-b) v0 + sigma(b-a) v1 with a, b the scaled scores
+    k2 = r.normal(size=(2, 4))
+    o, l = oracle.attention_rows(q, k2, v[:2], 0.3)
+    a, b = 0.3 * (q @ k2[0]), 0.3 * (q @ k2[1])
+    w0 = 1 / (1 + np.exp(b - a))
+    assert np.abs(o - (w0[:, None] * v[0] + (1 - w0)[:, None] * v[1])).max() < TIGHT
+    assert np.abs(l - np.logaddexp(a, b)).max() < TIGHT
+    # very sharp softmax picks the arg-max key
+    k = r.normal(size=(9, 4))
+    o, _ = oracle.attention_rows(q, k, v, 1e4)
+    assert np.abs(o - v[np.argmax(q @ k.T, axis=1)]).max() < 1e-9
+
+
+def test_algebraic_invariants():
+    r = rng(6)
+    q, k, v = r.normal(size=(7, 5)), r.normal(size=(10, 5)), r.normal(size=(10, 4))
+    s = 0.6
+    o, l = oracle.attention_rows(q, k, v, s)
+    perm = r.permutation(10)
+    op, lp = oracle.attention_rows(q, k[perm], v[perm], s)
+    assert np.abs(o - op).max() < TIGHT and np.abs(l - lp).max() < TIGHT
+    u = r.normal(size=5)
+    os_, ls = oracle.attention_rows(q, k + u, v, s)
+    assert np.abs(o - os_).max() < 1e-11 and np.abs(ls - (l + s * (q @ u))).max() < 1e-11
+    v2 = r.normal(size=(10, 4))
+    o2, _ = oracle.attention_rows(q, k, v2, s)
+    o3, _ = oracle.attention_rows(q, k, 2.5 * v - 0.5 * v2, s)
+    assert np.abs(o3 - (2.5 * o - 0.5 * o2)).max() < 1e-11
+
+
+def test_scale_matters():
+    r = rng(7)
+    q, k, v = r.normal(size=(4, 8)), r.normal(size=(6, 8)), r.normal(size=(6, 2))
+    o1, l1 = oracle.attention_rows(q, k, v, 1 / math.sqrt(8))
+    o2, l2 = oracle.attention_rows(q * (1 / math.sqrt(8)), k, v, 1.0)
+    assert np.abs(o1 - o2).max() < TIGHT and np.abs(l1 - l2).max() < TIGHT
+    o3, _ = oracle.attention_rows(q, k, v, 1.0)
+    assert np.abs(o1 - o3).max() > 1e-3
+
+
+def test_bf16_upcast_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F80, 0xFF80], dtype=np.uint16)
+    x = oracle.bf16_bits_to_f64(bits)
+    assert x[0] == 1.0 and x[1] == -2.0 and x[2] == 1.0078125
+    assert x[3] == 2.0 ** -133 and x[4] == np.inf and x[5] == -np.inf
+
+
+# ----------------------------------------------------------------- structural reductions
+
+def test_varlen_is_per_sequence_dense():
+    r = rng(8)
+    cu = np.array([0, 3, 7], dtype=np.int32)     # the page's example (section 3.3)
+    H, d = 2, 4
+    q, k, v = (r.normal(size=(7, H, d)) for _ in range(3))
+    for causal in (False, True):
+        o, l = oracle.attention_varlen(q, k, v, cu, cu, 0.5, causal)
+        for a, b in ((0, 3), (3, 7)):
+            for h in range(H):
+                od, ld = oracle.attention_rows(q[a:b, h], k[a:b, h], v[a:b, h], 0.5, causal)
+                assert np.abs(o[a:b, h] - od).max() == 0 and np.abs(l[a:b, h] - ld).max() == 0
+    # tokens of one sequence never see another sequence's keys
+    k2 = k.copy()
+    k2[3:] += 100
+    o2, _ = oracle.attention_varlen(q, k2, v, cu, cu, 0.5, False)
+    o1, _ = oracle.attention_varlen(q, k, v, cu, cu, 0.5, False)
+    assert np.abs(o2[:3] - o1[:3]).max() == 0
+
+
+def test_varlen_q_shorter_than_k_bottom_right():
+    r = rng(9)
+    cq = np.array([0, 2, 5], dtype=np.int32)
+    ck = np.array([0, 6, 8], dtype=np.int32)
+    q, k, v = r.normal(size=(5, 1, 3)), r.normal(size=(8, 1, 3)), r.normal(size=(8, 1, 3))
+    o, l = oracle.attention_varlen(q, k, v, cq, ck, 1.0, True)
+    # seq 0: Lq=2, Lk=6 -> row t sees keys 0..t+4
+    for t in range(2):
+        od, _ = oracle.attention_rows(q[t:t + 1, 0], k[:t + 5, 0], v[:t + 5, 0], 1.0, False)
+        assert np.abs(o[t, 0] - od[0]).max() < TIGHT
+    # seq 1: Lq=3, Lk=2 -> row 0 sees nothing
+    assert np.all(o[2, 0] == 0) and np.isneginf(l[2, 0])
+
+
+def _paged_small(seed, ctx, page=4, H=2, d=3, identity=False):
+    r = rng(seed)
+    n = [(c + page - 1) // page for c in ctx]
+    P = sum(n)
+    perm = np.arange(P) if identity else r.permutation(P)
+    bt = np.full((len(ctx), max(n)), P, dtype=np.int32)
+    off = 0
+    for b, m in enumerate(n):
+        bt[b, :m] = perm[off:off + m]
+        off += m
+    kc = r.normal(size=(P + 1, page, H, d))
+    vc = r.normal(size=(P + 1, page, H, d))
+    kc[P] = np.nan
+    vc[P] = np.nan
+    q = r.normal(size=(len(ctx), H, d))
+    return q, kc, vc, bt, np.array(ctx, dtype=np.int32)
+
+
+def test_paged_decode_gathers_through_block_table():
+    q, kc, vc, bt, ctx = _paged_small(10, [1, 4, 5, 11, 16])
+    o, l = oracle.attention_decode_paged(q, kc, vc, bt, ctx, 0.7)
+    assert np.isfinite(o).all() and np.isfinite(l).all()   # never touches the NaN page
+    page = kc.shape[1]
+    for b, c in enumerate(ctx):
+        # brute-force gather token by token
+        ks = np.stack([kc[bt[b, t // page], t % page] for t in range(c)])
+        vs = np.stack([vc[bt[b, t // page], t % page] for t in range(c)])
+        for h in range(q.shape[1]):
+            ob, lb = _brute([q[b, h].tolist()], ks[:, h].tolist(), vs[:, h].tolist(), 0.7, False)
+            assert np.abs(o[b, h] - ob[0]).max() < TIGHT and abs(l[b, h] - lb[0]) < TIGHT
+
+
+def test_paged_identity_equals_contiguous_and_last_causal_row():
+    q, kc, vc, bt, ctx = _paged_small(11, [7, 9], identity=True)
+    o, l = oracle.attention_decode_paged(q, kc, vc, bt, ctx, 0.3)
+    page = kc.shape[1]
+    flat_k = kc[:-1].reshape(-1, *kc.shape[2:])
+    flat_v = vc[:-1].reshape(-1, *vc.shape[2:])
+    start = 0
+    for b, c in enumerate(ctx):
+        for h in range(q.shape[1]):
+            kk = flat_k[start:start + c, h]
+            vv = flat_v[start:start + c, h]
+            od, ld = oracle.attention_rows(q[b, h][None], kk, vv, 0.3, False)
+            assert np.abs(o[b, h] - od[0]).max() == 0 and l[b, h] == ld[0]
+            # decode == last row of a causal run whose last query is q
+            qq = np.concatenate([np.random.default_rng(0).normal(size=(c - 1, q.shape[2])), q[b, h][None]])
+            oc, lc = oracle.attention_rows(qq, kk, vv, 0.3, True)
+            assert np.abs(oc[-1] - od[0]).max() < TIGHT and abs(lc[-1] - ld[0]) < TIGHT
+        start += ((c + page - 1) // page) * page
+
+
+def test_dense_wrapper_layout():
+    r = rng(12)
+    q, k, v = (r.normal(size=(2, 3, 5, 4)) for _ in range(3))
+    o, l = oracle.attention_dense(q, k, v, 0.5, True)
+    for b in range(2):
+        for h in range(3):
+            od, ld = oracle.attention_rows(q[b, h], k[b, h], v[b, h], 0.5, True)
+            assert np.array_equal(o[b, h], od) and np.array_equal(l[b, h], ld)
+
+
+def test_optional_sdpa_crosscheck():
+    """Non-authoritative: PyTorch's CPU math SDPA in float64 agrees with the oracle."""
+    torch = pytest.importorskip("torch")
+    r = rng(13)
+    q, k, v = (r.normal(size=(1, 2, 33, 16)) for _ in range(3))
+    for causal in (False, True):
+        o, _ = oracle.attention_dense(q, k, v, 0.25, causal)
+        t = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.25)
+        assert np.abs(o - t.numpy()).max() < 1e-12
