@@ -1,0 +1,181 @@
+"""ctypes binding of libattn.so (the C ABI in include/attn.h).
+
+Argument marshalling only: torch tensors are turned into device pointers, sizes,
+strides and the current HIP stream, and passed to the library.  Every step of the
+computation runs in the library's kernels; there is no fallback of any kind.  If
+libattn.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
+
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
+           "attn_status_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so (once).  Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64p, i64p, i64p, i64p, f32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd_varlen.restype = i32
+    lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode_paged_workspace_size.restype = sz
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().attn_status_string(status).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides3(t):
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
+def _check(rc: int, where: str):
+    if rc != ATTN_OK:
+        raise AttnError(rc, where)
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
+             with_lse: bool = True, stream=None):
+    """Dense attention.  q [B, H, N, d], k/v [B, H, Nk, d] (bf16 or fp32, any strides
+    with a contiguous last dim).  Returns (o, lse) with o like q and lse float32
+    [B, H, N] (None when ``with_lse`` is false)."""
+    torch = _torch()
+    lib = load()
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if with_lse else None,
+                      B, H, N, Nk, d, _dtype_code(q), _strides3(q), _strides3(k), _strides3(v),
+                      _strides3(o), scale, int(bool(causal)), _stream(stream))
+    _check(rc, "attn_fwd")
+    return o, (lse if with_lse else None)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    scale: float | None = None, causal: bool = False, out=None, lse=None,
+                    with_lse: bool = True, stream=None):
+    """Packed variable-length attention.  q [total_q, H, d], k/v [total_k, H, d]
+    contiguous bf16; cu_seqlens_* int32 device tensors [num_seqs + 1].  Returns
+    (o [total_q, H, d], lse float32 [total_q, H])."""
+    torch = _torch()
+    lib = load()
+    tq, H, d = q.shape
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("varlen tensors must be contiguous [tokens, H, d]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != num_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((tq, H), dtype=torch.float32, device=q.device)
+    rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if with_lse else None,
+                             _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q),
+                             int(max_seqlen_k), H, d, _dtype_code(q), scale, int(bool(causal)),
+                             _stream(stream))
+    _check(rc, "attn_fwd_varlen")
+    return o, (lse if with_lse else None)
+
+
+def attn_decode_paged_workspace_size(B: int, H: int, d: int, max_context_len: int, page_size: int = 16) -> int:
+    return int(load().attn_decode_paged_workspace_size(B, H, d, max_context_len, page_size))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
+                      scale: float | None = None, workspace=None, out=None, lse=None,
+                      with_lse: bool = True, stream=None):
+    """Decode over a paged KV pool.  q [B, H, d]; k_cache/v_cache [num_pages, page, H, d]
+    bf16 contiguous; block_table int32 [B, max_pages]; context_lens int32 [B].
+    ``workspace`` (uint8 device tensor) is allocated here when not given.  Returns
+    (o [B, H, d], lse float32 [B, H])."""
+    torch = _torch()
+    lib = load()
+    B, H, d = q.shape
+    num_pages, page = k_cache.shape[0], k_cache.shape[1]
+    for t in (q, k_cache, v_cache, block_table, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_table and context_lens must be int32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = attn_decode_paged_workspace_size(B, H, d, int(max_context_len), page)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    if with_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    rc = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse) if with_lse else None,
+                               _ptr(block_table), block_table.shape[1], _ptr(context_lens), B, num_pages,
+                               page, H, d, int(max_context_len), scale, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "attn_decode_paged")
+    return o, (lse if with_lse else None)

@@ -1,0 +1,185 @@
+// Host side of libattn.so: argument validation, launch geometry and the C ABI
+// declared in include/attn.h.  Nothing here allocates device memory, synchronises a
+// stream or keeps state between calls.
+#include "../../include/attn.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+#include "attn_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634074f;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int fail(attn_status s) { return static_cast<int>(s); }
+
+inline bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
+
+// Strides (b, h, n) of a tensor, defaulting to contiguous [B, H, N, d].
+inline void strides_or_default(const int64_t* s, int H, int N, int d, int64_t out[3]) {
+  if (s) {
+    out[0] = s[0];
+    out[1] = s[1];
+    out[2] = s[2];
+  } else {
+    out[2] = d;
+    out[1] = (int64_t)N * d;
+    out[0] = (int64_t)H * N * d;
+  }
+}
+
+// Every row start must be 16-byte aligned for the vector loads/stores.
+inline bool strides_aligned(const int64_t s[3], int esize) {
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || ((s[i] * esize) & 15) != 0) return false;
+  return true;
+}
+
+inline int check_launch(hipError_t e) {
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH);
+  if (getenv("ATTN_DEBUG") != nullptr) {
+    // test aid: surface asynchronous faults at the call that caused them
+    if (hipDeviceSynchronize() != hipSuccess || hipGetLastError() != hipSuccess) return fail(ATTN_ERR_LAUNCH);
+  }
+  return ATTN_OK;
+}
+
+inline int n_splits(int max_ctx) { return (max_ctx + attn::kDecodeSplit - 1) / attn::kDecodeSplit; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 100; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int Nk, int d, int dtype,
+             const int64_t* q_strides, const int64_t* k_strides,
+             const int64_t* v_strides, const int64_t* o_strides,
+             float scale, int causal, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return fail(ATTN_ERR_UNSUPPORTED);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)B * H * N == 0) return ATTN_OK;  // no query rows: nothing to write
+  if (!q || !o || (Nk > 0 && (!k || !v))) return fail(ATTN_ERR_INVALID_ARG);
+  const int esize = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  strides_or_default(q_strides, H, N, d, qs);
+  strides_or_default(k_strides, H, Nk, d, ks);
+  strides_or_default(v_strides, H, Nk, d, vs);
+  strides_or_default(o_strides, H, N, d, os);
+  if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(ATTN_ERR_UNSUPPORTED);
+  if (!strides_aligned(qs, esize) || !strides_aligned(ks, esize) || !strides_aligned(vs, esize) ||
+      !strides_aligned(os, esize))
+    return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sn = qs[2];
+  p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sn = ks[2];
+  p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sn = vs[2];
+  p.o_sb = os[0]; p.o_sh = os[1]; p.o_sn = os[2];
+  p.l_sb = (int64_t)H * N; p.l_sh = N; p.l_sn = 1;
+  p.B = B; p.H = H; p.Nq = N; p.Nk = Nk;
+  p.scale_log2 = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_DTYPE_BF16) {
+    p.n_rb = (N + attn::kFwdBM - 1) / attn::kFwdBM;
+    return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, false, s));
+  }
+  p.n_rb = (N + attn::kFwdF32BM - 1) / attn::kFwdF32BM;
+  return check_launch(attn::launch_fwd_f32(p, d, causal != 0, s));
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
+                    int max_seqlen_q, int max_seqlen_k, int H, int d, int dtype,
+                    float scale, int causal, void* stream) {
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || H < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)num_seqs * H * max_seqlen_q == 0) return ATTN_OK;
+  if (!q || !o || !cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID_ARG);
+  if (max_seqlen_k > 0 && (!k || !v)) return fail(ATTN_ERR_INVALID_ARG);
+  if (!aligned16(q) || !aligned16(o) || (max_seqlen_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  const int64_t tok = (int64_t)H * d;
+  p.q_sn = tok; p.q_sh = d;
+  p.k_sn = tok; p.k_sh = d;
+  p.v_sn = tok; p.v_sh = d;
+  p.o_sn = tok; p.o_sh = d;
+  p.l_sn = H; p.l_sh = 1;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.B = num_seqs; p.H = H; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.n_rb = (max_seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM;
+  p.scale_log2 = scale * kLog2e;
+  return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len, int page_size) {
+  (void)page_size;
+  if (B <= 0 || H <= 0 || max_context_len <= 0 || (d != 64 && d != 128)) return 0;
+  const size_t slots = (size_t)B * H * n_splits(max_context_len);
+  return slots * (size_t)d * sizeof(float) + slots * 2 * sizeof(float);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* block_table, int max_pages_per_seq,
+                      const int32_t* context_lens, int B, int num_pages, int page_size,
+                      int H, int d, int max_context_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0 || max_context_len < 0)
+    return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if (page_size <= 0 || (page_size % 16) != 0) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)B * H == 0) return ATTN_OK;
+  if (!q || !o || !context_lens) return fail(ATTN_ERR_INVALID_ARG);
+  if (!aligned16(q) || !aligned16(o)) return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  if (max_context_len > 0) {
+    if (!k_cache || !v_cache || !block_table) return fail(ATTN_ERR_INVALID_ARG);
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(ATTN_ERR_UNSUPPORTED);
+    if ((int64_t)max_pages_per_seq * page_size < max_context_len) return fail(ATTN_ERR_INVALID_ARG);
+  }
+  const size_t need = attn_decode_paged_workspace_size(B, H, d, max_context_len, page_size);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(ATTN_ERR_INVALID_ARG);
+
+  attn::DecodeParams p{};
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.o = o; p.lse = lse;
+  p.block_table = block_table; p.context_lens = context_lens;
+  p.B = B; p.H = H; p.max_pages = max_pages_per_seq; p.page_size = page_size;
+  p.split_len = attn::kDecodeSplit;
+  p.max_splits = max_context_len > 0 ? n_splits(max_context_len) : 0;
+  const size_t slots = (size_t)B * H * p.max_splits;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_acc ? p.ws_acc + slots * d : nullptr;
+  p.scale_log2 = scale * kLog2e;
+  return check_launch(attn::launch_decode_paged(p, d, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

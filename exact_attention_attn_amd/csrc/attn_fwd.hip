@@ -1,0 +1,437 @@
+// Tiled exact-attention forward for gfx950 (MI355X): dense and variable-length.
+//
+// Method: "From standard Attention to FlashAttention and paged execution"
+// (dlog.com.cn), sections 2.1-2.3: Q is cut into row blocks that are independent
+// work units; each block streams every K/V column block through on-chip memory;
+// an online softmax (running max m, running sum l) rescales the accumulator so that
+// only O and the per-row logsumexp are written.  Each wavefront owns its own query
+// rows for the whole key loop, so no softmax state is ever exchanged between
+// wavefronts (section 2.3, the FA2 split).
+//
+// gfx950 mapping (bf16 kernel):
+//  * workgroup = NW wavefronts x 32 query rows; key tiles of 64.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows read from LDS, B = Q held in
+//    VGPRs for the whole loop.  In the 32x32 accumulator each lane then owns ONE
+//    query (column) and 16 keys, so the row max / row sum are 15 in-lane ops plus a
+//    single exchange with lane^32.
+//  * O^T += V^T P^T on the same MFMA: P^T is taken straight from the S^T
+//    accumulator (converted to bf16) as the B operand; the order in which keys enter
+//    the contraction follows the accumulator's layout, and V^T is read from LDS in
+//    that same order.  The O^T accumulator again gives each lane one query row, so
+//    the per-row rescale by exp(m_old - m_new) is a per-lane scalar multiply.
+//  * K tile: LDS row-major [key][d] (+16 B pad per row).  V tile: stored transposed
+//    [d][key] (+8 B pad) so that each lane reads 4 consecutive keys of one column with
+//    one 8-byte LDS read; the transpose happens while staging (dword global loads of
+//    whole V rows, byte permutes, 8-byte LDS stores).
+//  * The next K/V tile is fetched into registers while the current one is computed.
+//  * Scores are kept in base-2 units: p = exp2(s * scale*log2(e) - m2), using the
+//    hardware exp2.
+//
+// The fp32 kernel (used for float32 inputs) is a plain VALU version of the same
+// recurrence: 4 lanes per query row, K/V tiles broadcast from LDS.
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int BN = 64;  // keys per tile
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Block index -> (row block, batch/sequence, head).  Blocks that share (b, h) are
+// H*B apart, so with round-robin dispatch over the 8 XCDs all row blocks of one head
+// land on the same XCD (and its L2) whenever H*B is a multiple of 8.  Causal launches
+// hand out the heaviest (last) row blocks first.
+template <bool CAUSAL>
+__device__ __forceinline__ void block_coords(const FwdParams& p, int& rb, int& b, int& h) {
+  const int nhb = p.H * p.B;
+  const int bid = blockIdx.x;
+  const int hb = bid % nhb;
+  const int rbi = bid / nhb;
+  b = hb / p.H;
+  h = hb - b * p.H;
+  rb = CAUSAL ? (p.n_rb - 1 - rbi) : rbi;
+}
+
+template <bool VARLEN>
+__device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int h, int& Lq, int& Lk,
+                                           int64_t& qoff, int64_t& koff, int64_t& voff,
+                                           int64_t& ooff, int64_t& loff) {
+  if (VARLEN) {
+    const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
+    const int k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+    Lq = q1 - q0;
+    Lk = k1 - k0;
+    qoff = (int64_t)q0 * p.q_sn + (int64_t)h * p.q_sh;
+    koff = (int64_t)k0 * p.k_sn + (int64_t)h * p.k_sh;
+    voff = (int64_t)k0 * p.v_sn + (int64_t)h * p.v_sh;
+    ooff = (int64_t)q0 * p.o_sn + (int64_t)h * p.o_sh;
+    loff = (int64_t)q0 * p.l_sn + (int64_t)h * p.l_sh;
+  } else {
+    Lq = p.Nq;
+    Lk = p.Nk;
+    qoff = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    koff = (int64_t)b * p.k_sb + (int64_t)h * p.k_sh;
+    voff = (int64_t)b * p.v_sb + (int64_t)h * p.v_sh;
+    ooff = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+    loff = (int64_t)b * p.l_sb + (int64_t)h * p.l_sh;
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// bf16 MFMA kernel
+// ----------------------------------------------------------------------------------
+template <int D, int NW, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
+  constexpr int BM = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int KS = D + 8;   // K tile row stride, elements (16-byte aligned rows)
+  constexpr int VS = BN + 4;  // V^T tile row stride, elements (8-byte aligned rows)
+  constexpr int NK = BN * (D / 8) / NT;   // 16-byte K chunks per thread
+  constexpr int NV = 16 * (D / 2) / NT;   // (4-key group, column pair) items per thread
+  constexpr int DT = D / 16;              // k-steps of the S^T contraction
+  constexpr int DB = D / 32;              // 32-wide column blocks of O^T
+  static_assert(NK * NT == BN * (D / 8) && NV * NT == 16 * (D / 2), "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int rb, b, h;
+  block_coords<CAUSAL>(p, rb, b, h);
+  int Lq, Lk;
+  int64_t qoff, koff, voff, ooff, loff;
+  seq_bounds<VARLEN>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
+  const int row0 = rb * BM;
+  if (row0 >= Lq) return;  // uniform over the workgroup (varlen: sequence shorter)
+
+  const int shift = Lk - Lq;  // bottom-right causal alignment
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
+  const int ntiles = (kend + BN - 1) / BN;
+
+  const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + qoff;
+  const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + koff;
+  const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + voff;
+
+  const int wrow0 = row0 + wave * 32;  // first query row of this wavefront
+  const int qi = wrow0 + col;          // this lane's query row
+
+  // Q operand (B of S^T): lane (col, half) holds Q[qi][16t + 8half .. +8]
+  bf16x8 qreg[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (qi < Lq) u = *(const u32x4*)(Qg + (int64_t)qi * p.q_sn + 16 * t + 8 * half);
+    qreg[t] = as_bf16x8(u);
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m2 = kNegInf;  // running max, base-2 units
+  float l = 0.f;       // running sum
+
+  u32x4 kst[NK];
+  unsigned vst[NV][4];
+
+  auto load_tile = [&](int j) {
+    const int kt0 = j * BN;
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+      const int idx = tid + it * NT;
+      const int key = idx / (D / 8), ch = idx % (D / 8);
+      const int gk = kt0 + key;
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (gk < Lk) u = *(const u32x4*)(Kg + (int64_t)gk * p.k_sn + ch * 8);
+      kst[it] = u;
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int idx = tid + it * NT;
+      const int pp = idx % (D / 2), kg = idx / (D / 2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gk = kt0 + 4 * kg + r;
+        unsigned w = 0u;
+        if (gk < Lk) w = *(const unsigned*)(Vg + (int64_t)gk * p.v_sn + 2 * pp);
+        vst[it][r] = w;
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < NK; ++it) {
+      const int idx = tid + it * NT;
+      const int key = idx / (D / 8), ch = idx % (D / 8);
+      *(u32x4*)(Ks + key * KS + ch * 8) = kst[it];
+    }
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int idx = tid + it * NT;
+      const int pp = idx % (D / 2), kg = idx / (D / 2);
+      const unsigned w0 = vst[it][0], w1 = vst[it][1], w2 = vst[it][2], w3 = vst[it][3];
+      // low halves = column 2pp, high halves = column 2pp+1; 4 consecutive keys each
+      u32x2 lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
+      u32x2 hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
+      *(u32x2*)(Vt + (2 * pp) * VS + 4 * kg) = lo;
+      *(u32x2*)(Vt + (2 * pp + 1) * VS + 4 * kg) = hi;
+    }
+  };
+
+  const float c2 = p.scale_log2;
+
+  if (ntiles > 0) load_tile(0);
+  for (int j = 0; j < ntiles; ++j) {
+    if (j > 0) __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile(j + 1);
+
+    const int kt0 = j * BN;
+    // wavefront-uniform: every key of this tile is above every row of this wavefront
+    if (CAUSAL && kt0 > wrow0 + 31 + shift) continue;
+
+    // ---- S^T = K Q^T (64 keys x 32 queries, two 32x32 blocks)
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(Ks + (32 * c + col) * KS + 16 * t + 8 * half));
+        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t], sacc[c], 0, 0, 0);
+      }
+    }
+
+    // ---- masking: tail keys and (causal) keys above the diagonal
+    const bool need_mask = (kt0 + BN > Lk) || (CAUSAL && kt0 + BN - 1 > wrow0 + shift);
+    if (need_mask) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt0 + 32 * c + 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
+          if (!ok) sacc[c][v] = kNegInf;
+        }
+      }
+    }
+
+    // ---- online softmax (one query per lane; the other half-wave holds the rest)
+    float mx = kNegInf;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][v]);
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(m2, mx * c2);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;  // no admissible key yet: p = 0
+    const float alpha = exp2_fast(m2 - muse);            // m2 = -inf -> 0
+    float rs = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = exp2_fast(__builtin_fmaf(sacc[c][v], c2, -muse));
+        sacc[c][v] = pv;
+        rs += pv;
+      }
+    rs += xor32(rs);
+    l = l * alpha + rs;
+    m2 = mnew;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+
+    // ---- P^T as the B operand (bf16, round to nearest even)
+    bf16x8 pb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint16_t* vrow = Vt + (32 * db + col) * VS + 4 * half;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x2 lo = *(const u32x2*)(vrow + 16 * t);
+        const u32x2 hi = *(const u32x2*)(vrow + 16 * t + 8);
+        const u32x4 u = {lo.x, lo.y, hi.x, hi.y};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[t], oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
+  if (qi < Lq) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    uint16_t* Og = (uint16_t*)p.o + ooff + (int64_t)qi * p.o_sn;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __bf16 r0 = (__bf16)(oacc[db][4 * i + 0] * inv);
+        __bf16 r1 = (__bf16)(oacc[db][4 * i + 1] * inv);
+        __bf16 r2 = (__bf16)(oacc[db][4 * i + 2] * inv);
+        __bf16 r3 = (__bf16)(oacc[db][4 * i + 3] * inv);
+        const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
+        const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
+        *(u32x2*)(Og + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// fp32 VALU kernel (dense only): 64 query rows per workgroup, 4 lanes per row.
+// ----------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
+  constexpr int DL = D / 4;   // columns per lane
+  constexpr int KT = 32;      // keys per LDS tile
+  constexpr int RS = D + 4;   // LDS row stride (floats)
+  __shared__ __attribute__((aligned(16))) float Ksh[KT * RS];
+  __shared__ __attribute__((aligned(16))) float Vsh[KT * RS];
+
+  const int tid = threadIdx.x;
+  const int row = tid >> 2;
+  const int part = tid & 3;
+  int rb, b, h;
+  block_coords<CAUSAL>(p, rb, b, h);
+  int Lq, Lk;
+  int64_t qoff, koff, voff, ooff, loff;
+  seq_bounds<false>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
+  const int row0 = rb * kFwdF32BM;
+  if (row0 >= Lq) return;
+  const int shift = Lk - Lq;
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, max(0, row0 + kFwdF32BM + shift));
+  const int ntiles = (kend + KT - 1) / KT;
+
+  const float* Qg = (const float*)p.q + qoff;
+  const float* Kg = (const float*)p.k + koff;
+  const float* Vg = (const float*)p.v + voff;
+  const int qi = row0 + row;
+
+  float q[DL], o[DL];
+#pragma unroll
+  for (int c = 0; c < DL; ++c) {
+    q[c] = qi < Lq ? Qg[(int64_t)qi * p.q_sn + part * DL + c] : 0.f;
+    o[c] = 0.f;
+  }
+  float m2 = kNegInf, l = 0.f;
+  const float c2 = p.scale_log2;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kt0 = j * KT;
+    __syncthreads();
+    for (int idx = tid; idx < KT * (D / 4); idx += 256) {
+      const int key = idx / (D / 4), c4 = idx % (D / 4);
+      const int gk = kt0 + key;
+      float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (gk < Lk) {
+        kv = *(const float4*)(Kg + (int64_t)gk * p.k_sn + 4 * c4);
+        vv = *(const float4*)(Vg + (int64_t)gk * p.v_sn + 4 * c4);
+      }
+      *(float4*)(Ksh + key * RS + 4 * c4) = kv;
+      *(float4*)(Vsh + key * RS + 4 * c4) = vv;
+    }
+    __syncthreads();
+
+    float s[KT];
+    float mx = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < KT; ++jj) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) acc = __builtin_fmaf(q[c], Ksh[jj * RS + part * DL + c], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      const int key = kt0 + jj;
+      const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
+      s[jj] = ok ? acc : kNegInf;
+      mx = fmaxf(mx, s[jj]);
+    }
+    const float mnew = fmaxf(m2, mx * c2);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = exp2f(m2 - muse);
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < KT; ++jj) {
+      s[jj] = exp2f(__builtin_fmaf(s[jj], c2, -muse));
+      rs += s[jj];
+    }
+    l = l * alpha + rs;
+    m2 = mnew;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) {
+      float acc = o[c] * alpha;
+#pragma unroll
+      for (int jj = 0; jj < KT; ++jj) acc = __builtin_fmaf(s[jj], Vsh[jj * RS + part * DL + c], acc);
+      o[c] = acc;
+    }
+  }
+
+  if (qi < Lq) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float* Og = (float*)p.o + ooff + (int64_t)qi * p.o_sn + part * DL;
+#pragma unroll
+    for (int c = 0; c < DL; ++c) Og[c] = o[c] * inv;
+    if (p.lse != nullptr && part == 0)
+      p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_bf16_t(const FwdParams& p, hipStream_t s) {
+  constexpr int NW = kFwdBM / 32;
+  const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
+  if (nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32_t(const FwdParams& p, hipStream_t s) {
+  const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
+  if (nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s) {
+  if (d == 128) {
+    if (varlen) return causal ? launch_bf16_t<128, true, true>(p, s) : launch_bf16_t<128, false, true>(p, s);
+    return causal ? launch_bf16_t<128, true, false>(p, s) : launch_bf16_t<128, false, false>(p, s);
+  }
+  if (varlen) return causal ? launch_bf16_t<64, true, true>(p, s) : launch_bf16_t<64, false, true>(p, s);
+  return causal ? launch_bf16_t<64, true, false>(p, s) : launch_bf16_t<64, false, false>(p, s);
+}
+
+hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return causal ? launch_f32_t<128, true>(p, s) : launch_f32_t<128, false>(p, s);
+  return causal ? launch_f32_t<64, true>(p, s) : launch_f32_t<64, false>(p, s);
+}
+
+}  // namespace attn

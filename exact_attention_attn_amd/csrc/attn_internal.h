@@ -1,0 +1,65 @@
+// Internal declarations shared by the host entry points and the kernel launchers of
+// libattn.so.  Not part of the C ABI (that is include/attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Parameters of one dense or varlen forward launch.  Strides are in elements.
+// Dense: tensor (b, h, n, :) starts at b*sb + h*sh + n*sn.
+// Varlen: token t of head h starts at t*sn + h*sh (sb unused); sequence s owns
+// tokens [cu[s], cu[s+1]).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t l_sb, l_sh, l_sn;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B;      // batch (dense) or number of sequences (varlen)
+  int H;
+  int Nq;     // dense: query length; varlen: max_seqlen_q
+  int Nk;     // dense: key length;   varlen: max_seqlen_k
+  int n_rb;   // query row blocks per (b, h)
+  float scale_log2;  // scale * log2(e): scores are handled in base-2 units
+};
+
+struct DecodeParams {
+  const void* q;        // [B, H, d]
+  const void* k_cache;  // [P, page, H, d]
+  const void* v_cache;
+  void* o;              // [B, H, d]
+  float* lse;           // [B, H] or null
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* context_lens; // [B]
+  float* ws_acc;        // [B, H, max_splits, d]   unnormalised partial outputs
+  float* ws_ml;         // [B, H, max_splits, 2]   partial (m, l), base-2 units
+  int B, H;
+  int max_pages;
+  int page_size;
+  int split_len;        // tokens per split, a multiple of 16
+  int max_splits;
+  float scale_log2;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
+
+// Row-block height of the bf16 forward kernel (query rows per workgroup).
+constexpr int kFwdBM = 128;
+// Row-block height of the fp32 forward kernel.
+constexpr int kFwdF32BM = 64;
+// Tokens per decode split.
+constexpr int kDecodeSplit = 512;
+
+}  // namespace attn

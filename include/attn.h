@@ -1,0 +1,135 @@
+/*
+ * attn.h — C ABI of libattn.so: exact attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * Three entry points, one per way the attention library is called on the
+ * dlog.com.cn page "From standard Attention to FlashAttention and paged execution":
+ *
+ *   attn_fwd            fixed-length batched attention (section 3.1, the basic
+ *                       fixed-length interface), layout [B, H, N, d] by default;
+ *   attn_fwd_varlen     variable-length packed batch described by cumulative
+ *                       sequence lengths (section 3.3, cu_seqlens);
+ *   attn_decode_paged   one new query token per sequence attending its cached
+ *                       K/V, read page by page through a block table
+ *                       (sections 3.4 and "PagedAttention").
+ *
+ * Each computes, per query row i, O_i = sum_j softmax_j(scale * q_i . k_j) v_j over
+ * the admissible keys j, and the row's logsumexp lse_i = ln sum_j exp(scale * q_i . k_j)
+ * (the statistic the tiled forward keeps for the backward pass: "L2.5 SOTA Kernel",
+ * yulong.wang, sections 2.1 and 2.3).  S and P never reach memory.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - Every pointer argument except the stride arrays is a DEVICE pointer, allocated
+ *   and owned by the caller.  The library allocates nothing, frees nothing and keeps
+ *   no state between calls; calls are reentrant and thread-safe.
+ * - Element types: ATTN_DTYPE_BF16 (raw bfloat16) or ATTN_DTYPE_F32.  lse is always
+ *   float32.  Accumulation is float32.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL means
+ *   the null stream).  Results are valid once the caller has synchronised that stream.
+ * - Arguments are validated on the host before any launch; an invalid call returns a
+ *   non-zero status and launches nothing.  Device-array CONTENTS (cu_seqlens,
+ *   block_table, context_lens) are the caller's contract and are not checked: reading
+ *   them would need a device-to-host copy.
+ * - Causal masking: key j is admissible for query row i iff j <= i + (Lk - Lq)
+ *   (bottom-right alignment; j <= i when Lq == Lk).  A row with no admissible key
+ *   gets O = 0 and lse = -inf.
+ * - Supported head dimension d: 64 or 128.  Other values are rejected
+ *   (ATTN_ERR_UNSUPPORTED), never computed on a truncated tile.
+ * - scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale, short workspace */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d, dtype, alignment, page size) */
+  ATTN_ERR_LAUNCH = 3       /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+/*
+ * attn_fwd — dense batched attention.
+ *
+ * q, o : logical [B, H, N, d];  k, v : logical [B, H, Nk, d]; element type `dtype`
+ *        (o has q's type).  The d dimension must be contiguous.
+ * *_strides : three int64 element strides for the (b, h, n) dimensions of that tensor,
+ *        or NULL for a contiguous [B, H, N(k), d] tensor.  Strides make the
+ *        [B, N, H, d] layout of the flash-attn interface and packed QKV / KV
+ *        tensors ([B, N, 3, H, d], [B, N, 2, H, d]; page section 3.2) usable
+ *        without copies.  Every row start must be 16-byte aligned.
+ * lse  : float32 [B, H, N] contiguous, or NULL to skip it.
+ * causal : 0 or 1 (bottom-right aligned when N != Nk).
+ * B, H, N, Nk may be 0 (nothing is launched).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int Nk, int d, int dtype,
+             const int64_t* q_strides, const int64_t* k_strides,
+             const int64_t* v_strides, const int64_t* o_strides,
+             float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_varlen — packed variable-length batch (bfloat16).
+ *
+ * q, o : [total_q, H, d] contiguous;  k, v : [total_k, H, d] contiguous.
+ * cu_seqlens_q, cu_seqlens_k : int32 [num_seqs + 1] device arrays of prefix sums;
+ *        sequence s owns Q rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and K/V rows
+ *        [cu_seqlens_k[s], cu_seqlens_k[s+1]) (the page's example [0, 3, 7] is two
+ *        sequences of 3 and 4 tokens).  Sequences never attend to each other.
+ * max_seqlen_q / max_seqlen_k : upper bounds of the per-sequence lengths (they size
+ *        the launch grid; a smaller value than the truth is a contract violation).
+ * lse  : float32 [total_q, H], or NULL.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
+                    int max_seqlen_q, int max_seqlen_k, int H, int d, int dtype,
+                    float scale, int causal, void* stream);
+
+/*
+ * attn_decode_paged_workspace_size — bytes of device workspace attn_decode_paged
+ * needs for this batch shape (0 when nothing needs to be launched).
+ */
+size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len, int page_size);
+
+/*
+ * attn_decode_paged — decode step over a paged KV cache (bfloat16).
+ *
+ * q, o : [B, H, d] contiguous (one new query token per sequence).
+ * k_cache, v_cache : [num_pages, page_size, H, d] contiguous page pools.
+ * block_table : int32 [B, max_pages_per_seq]; token t of sequence b lives in page
+ *        block_table[b][t / page_size], slot t % page_size.  Entries past
+ *        ceil(context_lens[b] / page_size) are never read.
+ * context_lens : int32 [B], each in [0, max_context_len]; sequence b's query attends
+ *        its keys [0, context_lens[b]) (with one query token, causal and non-causal
+ *        coincide).  Slots past the context in the last page are never read.
+ * page_size : a positive multiple of 16.
+ * lse  : float32 [B, H], or NULL.
+ * workspace : device buffer of at least attn_decode_paged_workspace_size(...) bytes,
+ *        owned by the caller; its contents on entry do not matter.  Concurrent calls
+ *        must not share one workspace.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* block_table, int max_pages_per_seq,
+                      const int32_t* context_lens, int B, int num_pages, int page_size,
+                      int H, int d, int max_context_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

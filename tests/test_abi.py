@@ -1,0 +1,140 @@
+"""The C ABI: the library loads, exports every function the header declares, and
+rejects invalid requests on the host before any launch (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_attn_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entries():
+    names = header_functions()
+    for n in ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.load()
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    assert set(header_functions()) == set(attn.EXPORTS)
+    assert lib.attn_version() >= 100
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 2)
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=64, Nk=64, d=128,
+             dtype=attn.ATTN_DTYPE_BF16, qs=None, ks=None, vs=None, os_=None, scale=0.1, causal=0)
+    a.update(kw)
+    return attn.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["Nk"],
+                                a["d"], a["dtype"], a["qs"], a["ks"], a["vs"], a["os_"], a["scale"],
+                                a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=3), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(N=-5), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(q=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(q=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(v=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(qs=(ctypes.c_int64 * 3)(64 * 128, 128 * 64, 129)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=(ctypes.c_int64 * 3)(-128, 128, 128)), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(lse=ctypes.c_void_p((1 << 20) + 1)), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), attn.ATTN_OK),          # nothing to do: no launch
+    (dict(N=0), attn.ATTN_OK),
+])
+def test_fwd_rejects_before_launch(kw, status):
+    assert fwd(**kw) == status
+
+
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cq=FAKE, ck=FAKE, S=2, mq=16, mk=16, H=2, d=128,
+             dtype=attn.ATTN_DTYPE_BF16, scale=0.1, causal=1)
+    a.update(kw)
+    return attn.load().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["S"],
+                                       a["mq"], a["mk"], a["H"], a["d"], a["dtype"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(cq=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ck=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(S=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(mq=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(q=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(S=0), attn.ATTN_OK),
+    (dict(mq=0), attn.ATTN_OK),
+])
+def test_varlen_rejects_before_launch(kw, status):
+    assert varlen(**kw) == status
+
+
+def decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, bt=FAKE, maxp=8, cl=FAKE, B=2, P=16, page=16, H=2,
+             d=128, maxctx=128, scale=0.1, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return attn.load().attn_decode_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["bt"], a["maxp"], a["cl"],
+                                         a["B"], a["P"], a["page"], a["H"], a["d"], a["maxctx"], a["scale"],
+                                         a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(page=24), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(page=0), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(wsb=16), attn.ATTN_ERR_INVALID_ARG),
+    (dict(bt=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(cl=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(maxp=4), attn.ATTN_ERR_INVALID_ARG),      # 4 pages * 16 < 128 tokens
+    (dict(B=-2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=-0.5), attn.ATTN_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(B=0), attn.ATTN_OK),
+])
+def test_decode_rejects_before_launch(kw, status):
+    assert decode(**kw) == status
+
+
+def test_workspace_size():
+    ws = attn.attn_decode_paged_workspace_size
+    assert ws(0, 32, 128, 8192, 16) == 0
+    assert ws(64, 32, 128, 0, 16) == 0
+    one = ws(1, 1, 128, 1, 16)
+    assert one == 130 * 4
+    assert ws(64, 32, 128, 8192, 16) == 64 * 32 * 16 * 130 * 4   # 512-token splits
+    assert ws(64, 32, 128, 8193, 16) == 64 * 32 * 17 * 130 * 4
+    assert ws(2, 2, 64, 100, 16) == 2 * 2 * 1 * 66 * 4
+
+
+def test_status_strings():
+    assert attn.status_string(0) == "ok"
+    assert "unsupported" in attn.status_string(2)
+    assert attn.status_string(99) == "unknown status"

@@ -1,0 +1,268 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on the same
+seeded inputs, element by element.  bf16 runs feed the oracle the same bf16 values.
+
+Small shapes are compared everywhere; the full workloads are compared on sampled
+rows the oracle computes one by one, in the launch configuration the bench times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.golden.load import load
+from tests.util import TOL_BF16_LSE, TOL_BF16_O, TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    import torch
+    import exact_attention_attn_amd as attn
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    attn.load()
+    return attn
+
+
+def run_dense(A, w, causal=None, layout="bhnd"):
+    import torch
+    causal = w.causal if causal is None else causal
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    if layout == "bnhd":   # same values, [B, N, H, d] memory order through strides
+        q = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def tol(w):
+    return (TOL_F32, TOL_F32) if w.dtype == "f32" else (TOL_BF16_O, TOL_BF16_LSE)
+
+
+# ------------------------------------------------------------------ page examples
+
+def test_hand_example_fp32(A):
+    """The dlog.com.cn section 2.1 example (N=2, d=3, scale 1), zero-padded to d=64:
+    zero columns change neither the scores nor O[:, :3]."""
+    import torch
+    g = load("hand_example.txt")
+    pad = lambda x: np.pad(x, ((0, 0), (0, 61))).astype(np.float32)[None, None]
+    q, k, v = (dev(pad(g[n])) for n in "QKV")
+    o, lse = A.attn_fwd(q, k, v, scale=1.0)
+    torch.cuda.synchronize()
+    e3, e2 = math.exp(3), math.exp(2)
+    P = np.array([[1 / (1 + e3), e3 / (1 + e3)], [1 / (1 + e2), e2 / (1 + e2)]])
+    assert_close("O", host(o)[0, 0, :, :3], P @ g["V"], TOL_F32)
+    assert np.all(host(o)[0, 0, :, 3:] == 0)
+    assert_close("lse", host(lse)[0, 0], np.array([5 + math.log1p(math.exp(-3)), 3 + math.log1p(math.exp(-2))]), TOL_F32)
+
+
+# ------------------------------------------------------------------ full workloads
+
+def test_c1_fp32_full(A):
+    w = synth.workload("c1")
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal)
+    assert_close("O", o, ro, TOL_F32)
+    assert_close("lse", lse, rl, TOL_F32)
+
+
+def _dense_sampled(A, w, pairs, rows):
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal, heads=pairs, rows=rows)
+    to, tl = tol(w)
+    assert_close("O", o, ro, to)
+    assert_close("lse", lse, rl, tl)
+    return o, lse
+
+
+def _rows(N, rng, extra=48):
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
+    r = set(x for x in fixed if 0 <= x < N) | set(rng.integers(0, N, extra).tolist())
+    return np.array(sorted(r))
+
+
+def test_c2_bf16_full_sampled(A):
+    w = synth.workload("c2")
+    rng = np.random.default_rng(100)
+    pairs = [(0, 0), (1, 7), (2, 15), (3, 3)]
+    _dense_sampled(A, w, pairs, _rows(w.N, rng))
+
+
+def test_c3_bf16_causal_full_sampled(A):
+    w = synth.workload("c3")
+    rng = np.random.default_rng(101)
+    pairs = [(0, 0), (0, 13), (0, 31)]
+    o, lse = _dense_sampled(A, w, pairs, _rows(w.N, rng))
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+def test_c4_varlen_full_sampled(A):
+    import torch
+    w = synth.workload("c4")
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    rng = np.random.default_rng(102)
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, heads=[0, 17, 31],
+                                     rows_per_seq=lambda s, L: _rows(L, rng, 12))
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+    assert np.isfinite(o).all()
+
+
+def test_c5_decode_full(A):
+    import torch
+    w = synth.workload("c5")
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), int(w.context_lens.max()), scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()   # no NaN page or tail slot was read
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale,
+                                           heads=[0, 9, 31])
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+# ------------------------------------------------------------------ edge cases, small shapes
+
+@pytest.mark.parametrize("N,Nk,causal", [(1, 1, False), (1, 1, True), (2, 2, True), (63, 63, True),
+                                         (65, 65, False), (129, 129, True), (200, 200, True),
+                                         (300, 300, False), (513, 513, True), (77, 300, True),
+                                         (300, 77, True), (300, 77, False), (128, 1, False),
+                                         (5, 1000, True)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_ragged_bf16(A, N, Nk, causal, d):
+    w = synth.dense(2, 3, N, d, "bf16", causal, seed=N * 7 + Nk, Nk=Nk)
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, causal)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+@pytest.mark.parametrize("N,Nk,causal,d", [(1, 1, False, 64), (100, 100, True, 64), (130, 70, True, 128),
+                                           (70, 130, True, 128), (257, 257, False, 128)])
+def test_dense_ragged_fp32(A, N, Nk, causal, d):
+    w = synth.dense(2, 2, N, d, "f32", causal, seed=N + 3 * Nk, Nk=Nk)
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, causal)
+    assert_close("O", o, ro, TOL_F32)
+    assert_close("lse", lse, rl, TOL_F32)
+
+
+def test_dense_strided_layout(A):
+    """[B, N, H, d] memory order passed through the stride arguments."""
+    w = synth.dense(2, 4, 190, 128, "bf16", True, seed=5)
+    o, lse = run_dense(A, w, layout="bnhd")
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, True)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+def test_dense_deterministic(A):
+    import torch
+    w = synth.dense(1, 8, 1000, 128, "bf16", True, seed=9)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o1, l1 = A.attn_fwd(q, k, v, causal=True)
+    o2, l2 = A.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_dense_causal_prefix_invariance(A):
+    """Changing K/V rows after row i leaves rows <= i bit-identical."""
+    import torch
+    w = synth.dense(1, 2, 500, 128, "bf16", True, seed=10)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o1, l1 = A.attn_fwd(q, k, v, causal=True)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 300:] = torch.randn_like(k2[:, :, 300:]) * 3
+    v2[:, :, 300:] = torch.randn_like(v2[:, :, 300:]) * 3
+    o2, l2 = A.attn_fwd(q, k2, v2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :300], o2[:, :, :300]) and torch.equal(l1[:, :, :300], l2[:, :, :300])
+    assert not torch.equal(o1[:, :, 300:], o2[:, :, 300:])
+
+
+@pytest.mark.parametrize("lens,lens_k,causal", [
+    ([3, 4], None, True), ([3, 4], None, False),
+    ([0, 1, 64, 65, 127, 128, 129, 300], None, True),
+    ([0, 1, 64, 65, 127, 128, 129, 300], None, False),
+    ([10, 200, 0, 7], [50, 200, 5, 0], True),
+    ([10, 200, 0, 7], [50, 200, 5, 0], False),
+    ([500], [1], True),
+])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_edges(A, lens, lens_k, causal, d):
+    import torch
+    w = synth.varlen(H=3, d=d, causal=causal, seed=len(lens) + d, lens=lens, lens_k=lens_k)
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, causal)
+    assert_close("O", host(o), ro, TOL_BF16_O)
+    assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
+def test_varlen_equals_dense_per_sequence(A):
+    import torch
+    w = synth.varlen(H=4, d=128, causal=True, seed=3, lens=[130, 257, 64])
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=True)
+    for s in range(3):
+        a, b = int(w.cu_q[s]), int(w.cu_q[s + 1])
+        qd = dev(np.ascontiguousarray(w.q[a:b].transpose(1, 0, 2))[None])
+        kd = dev(np.ascontiguousarray(w.k[a:b].transpose(1, 0, 2))[None])
+        vd = dev(np.ascontiguousarray(w.v[a:b].transpose(1, 0, 2))[None])
+        od, ld = A.attn_fwd(qd, kd, vd, scale=w.scale, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0].transpose(0, 1), o[a:b]) and torch.equal(ld[0].transpose(0, 1), lse[a:b])
+
+
+@pytest.mark.parametrize("ctx,page", [([1, 15, 16, 17, 0, 511, 512, 513, 1024, 1500], 16),
+                                      ([33, 64, 100, 0, 600], 32), ([2000, 3], 64)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_edges(A, ctx, page, d):
+    import torch
+    w = synth.paged(H=4, d=d, ctx=ctx, page=page, seed=len(ctx) + page)
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), int(max(ctx)), scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
+    assert_close("O", host(o), ro, TOL_BF16_O)
+    assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
+def test_decode_identity_table_equals_dense_last_row(A):
+    """Paged decode with pages in order == the last row of a causal dense run."""
+    import torch
+    ctx = [700, 129]
+    w = synth.paged(H=2, d=128, ctx=ctx, identity=True, poison=False, seed=4)
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), max(ctx), scale=w.scale)
+    torch.cuda.synchronize()
+    flat_k = w.k_cache[:-1].reshape(-1, 2, 128)
+    flat_v = w.v_cache[:-1].reshape(-1, 2, 128)
+    start = 0
+    for b, c in enumerate(ctx):
+        ro, rl = oracle.attention_rows(w.q[b, 0][None], flat_k[start:start + c, 0], flat_v[start:start + c, 0], w.scale)
+        assert_close("O", host(o)[b, 0], ro[0], TOL_BF16_O)
+        assert_close("lse", host(lse)[b, 0:1], rl, TOL_BF16_LSE)
+        start += ((c + 15) // 16) * 16
+
+
+def test_decode_deterministic(A):
+    import torch
+    w = synth.paged(B=8, H=8, d=128, ctx_min=100, ctx_max=3000, seed=6)
+    args = (dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table), dev(w.context_lens),
+            int(w.context_lens.max()))
+    o1, l1 = A.attn_decode_paged(*args, scale=w.scale)
+    o2, l2 = A.attn_decode_paged(*args, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -331,7 +331,7 @@ def test_paged_identity_equals_contiguous_and_last_causal_row():
             kk = flat_k[start:start + c, h]
             vv = flat_v[start:start + c, h]
             od, ld = oracle.attention_rows(q[b, h][None], kk, vv, 0.3, False)
-            assert np.abs(o[b, h] - od[0]).max() == 0 and l[b, h] == ld[0]
+            assert np.abs(o[b, h] - od[0]).max() < TIGHT and abs(l[b, h] - ld[0]) < TIGHT
             # decode == last row of a causal run whose last query is q
             qq = np.concatenate([np.random.default_rng(0).normal(size=(c - 1, q.shape[2])), q[b, h][None]])
             oc, lc = oracle.attention_rows(qq, kk, vv, 0.3, True)
