@@ -4,6 +4,7 @@
 #include "../../include/attn.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 
 #include "attn_internal.h"
@@ -89,6 +90,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
       !strides_aligned(os, esize))
     return fail(ATTN_ERR_UNSUPPORTED);
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  // key-tile byte offsets are 32-bit: 64 rows of K/V must span less than 2 GiB
+  if (64 * ks[2] * esize > INT32_MAX || 64 * vs[2] * esize > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED);
 
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;

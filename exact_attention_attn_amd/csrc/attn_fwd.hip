@@ -92,20 +92,47 @@ __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int h, int
 // ----------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ----------------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
-  constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int KS = D + 8;   // K tile row stride, elements (16-byte aligned rows)
-  constexpr int VS = BN + 4;  // V^T tile row stride, elements (8-byte aligned rows)
-  constexpr int NK = BN * (D / 8) / NT;   // 16-byte K chunks per thread
-  constexpr int NV = 16 * (D / 2) / NT;   // (4-key group, column pair) items per thread
-  constexpr int DT = D / 16;              // k-steps of the S^T contraction
-  constexpr int DB = D / 32;              // 32-wide column blocks of O^T
-  static_assert(NK * NT == BN * (D / 8) && NV * NT == 16 * (D / 2), "tile split");
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+// Deferred rescale: the reference max m2 (base-2 units) only moves when a row's new
+// maximum exceeds it by more than kRescaleSlack.  Probabilities are then bounded by
+// 2^kRescaleSlack instead of 1, which fp32 accumulators and bf16 operands carry
+// without loss; O = acc / l and lse = m2 + log2 l hold for any reference value, so
+// the result is the same function.  Most tiles then skip the O^T rescale.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFll ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+
+// 16-byte direct-to-LDS load per lane: lane i's data lands at lds + 16 i.  Kept out of
+// lambdas: the host pass would otherwise drop the kernel's launch stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
+}
+
+template <int D, int NW, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_bf16_kernel(const FwdParams p) {
+  constexpr int BM = 32 * NW;       // query rows per workgroup
+  constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
+  constexpr int DT = D / 16;        // k-steps of the S^T contraction
+  constexpr int DB = D / 32;        // 32-column blocks of O^T
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int NBLK = TILE_BYTES / 1024;   // 1 KiB direct-to-LDS blocks per K (or V) tile
+  constexpr int BPW = NBLK / NW;            // blocks per wavefront
+  static_assert(BPW * NW == NBLK, "tile split");
+  // LDS: two buffers, each [K tile | V tile]
+  //   K tile: [64 keys][CPR chunks], chunk c of key r stored at chunk c ^ (r % CPR)
+  //   V tile: [DB blocks][64 keys][4 chunks]  (32 columns of one key = 64 B)
+  // Two separate LDS objects (not one array indexed by parity): the compiler can then
+  // tell that reads of the current buffer do not alias the in-flight DMA into the other
+  // one, and does not stall them on the prefetch.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[2 * TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
   int64_t qoff, koff, voff, ooff, loff;
   seq_bounds<VARLEN>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
   const int row0 = rb * BM;
-  if (row0 >= Lq) return;  // uniform over the workgroup (varlen: sequence shorter)
+  if (row0 >= Lq) return;  // uniform over the workgroup
 
   const int shift = Lk - Lq;  // bottom-right causal alignment
   int kend = Lk;
@@ -129,11 +156,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
   const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + qoff;
   const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + koff;
   const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + voff;
+  const int64_t ksn = p.k_sn, vsn = p.v_sn;
 
-  const int wrow0 = row0 + wave * 32;  // first query row of this wavefront
-  const int qi = wrow0 + col;          // this lane's query row
+  const int wrow0 = row0 + wave * 32;
+  const int qi = wrow0 + col;
 
-  // Q operand (B of S^T): lane (col, half) holds Q[qi][16t + 8half .. +8]
   bf16x8 qreg[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -142,81 +169,62 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
     qreg[t] = as_bf16x8(u);
   }
 
+  // per-lane byte offsets of this wavefront's direct-to-LDS loads (relative to the tile's first key)
+  int kvoff[BPW], vvoff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int bi = wave * BPW + i;
+    {  // K block bi: keys (1024 / (2D)) * bi + lane / CPR, stored chunk lane % CPR
+      constexpr int KPB = 1024 / (2 * D);
+      const int key = KPB * bi + lane / CPR;
+      const int logical = (lane % CPR) ^ (key % CPR);
+      kvoff[i] = key * (int)ksn * 2 + logical * 16;
+    }
+    {  // V block bi: column block bi / 4, keys 16 * (bi % 4) + lane / 4, chunk lane % 4
+      const int db = bi / 4, key = 16 * (bi % 4) + lane / 4;
+      vvoff[i] = key * (int)vsn * 2 + (32 * db + 8 * (lane % 4)) * 2;
+    }
+  }
+
+  auto issue_tile = [&](int j, uint8_t* kb) {
+    const int kt0 = j * BN;
+    const int64_t krem = ((int64_t)(Lk - kt0 - 1) * ksn + D) * 2;  // bytes of valid keys from kt0 on
+    const int64_t vrem = ((int64_t)(Lk - kt0 - 1) * vsn + D) * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (int64_t)kt0 * ksn, krem);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (int64_t)kt0 * vsn, vrem);
+    uint8_t* vb = kb + TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = wave * BPW + i;
+      dma16(kr, kb + bi * 1024, kvoff[i]);
+      dma16(vr, vb + bi * 1024, vvoff[i]);
+    }
+  };
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m2 = kNegInf;  // running max, base-2 units
-  float l = 0.f;       // running sum
-
-  u32x4 kst[NK];
-  unsigned vst[NV][4];
-
-  auto load_tile = [&](int j) {
-    const int kt0 = j * BN;
-#pragma unroll
-    for (int it = 0; it < NK; ++it) {
-      const int idx = tid + it * NT;
-      const int key = idx / (D / 8), ch = idx % (D / 8);
-      const int gk = kt0 + key;
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (gk < Lk) u = *(const u32x4*)(Kg + (int64_t)gk * p.k_sn + ch * 8);
-      kst[it] = u;
-    }
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int idx = tid + it * NT;
-      const int pp = idx % (D / 2), kg = idx / (D / 2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gk = kt0 + 4 * kg + r;
-        unsigned w = 0u;
-        if (gk < Lk) w = *(const unsigned*)(Vg + (int64_t)gk * p.v_sn + 2 * pp);
-        vst[it][r] = w;
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < NK; ++it) {
-      const int idx = tid + it * NT;
-      const int key = idx / (D / 8), ch = idx % (D / 8);
-      *(u32x4*)(Ks + key * KS + ch * 8) = kst[it];
-    }
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int idx = tid + it * NT;
-      const int pp = idx % (D / 2), kg = idx / (D / 2);
-      const unsigned w0 = vst[it][0], w1 = vst[it][1], w2 = vst[it][2], w3 = vst[it][3];
-      // low halves = column 2pp, high halves = column 2pp+1; 4 consecutive keys each
-      u32x2 lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-      u32x2 hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-      *(u32x2*)(Vt + (2 * pp) * VS + 4 * kg) = lo;
-      *(u32x2*)(Vt + (2 * pp + 1) * VS + 4 * kg) = hi;
-    }
-  };
-
+  float m2 = kNegInf;  // reference max, base-2 units
+  float l = 0.f;
   const float c2 = p.scale_log2;
 
-  if (ntiles > 0) load_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    if (j > 0) __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1);
+  // LDS read offsets (bytes within a buffer)
+  const int ksw = col % CPR;
+  const int kread = col * (2 * D);                              // key = 32c + col, + c * 64 * D
+  const int vread = TILE_BYTES + (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
+  auto compute_tile = [&](int j, const uint8_t* kb) {
     const int kt0 = j * BN;
-    // wavefront-uniform: every key of this tile is above every row of this wavefront
-    if (CAUSAL && kt0 > wrow0 + 31 + shift) continue;
-
-    // ---- S^T = K Q^T (64 keys x 32 queries, two 32x32 blocks)
+    if (CAUSAL && kt0 > wrow0 + 31 + shift) return;  // whole tile above this wave's rows
+    // ---- S^T = K Q^T
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
+      const int off = kread + (((2 * t + half) ^ ksw) * 16);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(Ks + (32 * c + col) * KS + 16 * t + 8 * half));
-        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t], sacc[c], 0, 0, 0);
+        const u32x4 a = *(const lds_u32x4*)(kb + off + c * 64 * D);
+        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[t], sacc[c], 0, 0, 0);
       }
     }
 
@@ -224,26 +232,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
     const bool need_mask = (kt0 + BN > Lk) || (CAUSAL && kt0 + BN - 1 > wrow0 + shift);
     if (need_mask) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kt0 + 32 * c + 8 * (v >> 2) + 4 * half + (v & 3);
           const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
           if (!ok) sacc[c][v] = kNegInf;
         }
-      }
     }
 
-    // ---- online softmax (one query per lane; the other half-wave holds the rest)
+    // ---- online softmax with deferred rescale
     float mx = kNegInf;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][v]);
-    mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m2, mx * c2);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;  // no admissible key yet: p = 0
-    const float alpha = exp2_fast(m2 - muse);            // m2 = -inf -> 0
+    mx = fmaxf(mx, xor32(mx)) * c2;
+    const bool grow = mx > m2 + kRescaleSlack;  // also true on a row's first admissible key
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? mx : m2;
+      const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      m2 = mnew;
+    }
+    const float muse = (m2 == kNegInf) ? 0.f : m2;  // row without admissible key so far: p = 0
     float rs = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -253,11 +267,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
         sacc[c][v] = pv;
         rs += pv;
       }
-    rs += xor32(rs);
-    l = l * alpha + rs;
-    m2 = mnew;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+    l += rs + xor32(rs);
 
     // ---- P^T as the B operand (bf16, round to nearest even)
     bf16x8 pb[4];
@@ -266,18 +276,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; V^T operand through the LDS transposing read
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint16_t* vrow = Vt + (32 * db + col) * VS + 4 * half;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x2 lo = *(const u32x2*)(vrow + 16 * t);
-        const u32x2 hi = *(const u32x2*)(vrow + 16 * t + 8);
-        const u32x4 u = {lo.x, lo.y, hi.x, hi.y};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb[t], oacc[db], 0, 0, 0);
+        const uint8_t* vp = kb + vread + db * 4096 + t * 1024;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], oacc[db], 0, 0, 0);
       }
-    }
+  };
+
+  auto step = [&](int j, uint8_t* cur, uint8_t* nxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA into `cur` landed
+    __syncthreads();                                   // ... and every wave's; `nxt` is free
+    if (j + 1 < ntiles) issue_tile(j + 1, nxt);
+    compute_tile(j, cur);
+  };
+
+  if (ntiles > 0) issue_tile(0, smem0);
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, smem0, smem1);
+    if (j + 1 < ntiles) step(j + 1, smem1, smem0);
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
