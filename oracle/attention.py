@@ -144,13 +144,13 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, se
 
 
 def gather_paged(cache, block_table_row, ctx: int, page: int):
-    """Contiguous [ctx, H, d] view of one sequence's cached keys (or values): token t
+    """Contiguous [ctx, ...] copy of one sequence's cached keys (or values): token t
     lives in physical page block_table[t // page], slot t % page ("From standard
     Attention to FlashAttention and paged execution", sections "PagedAttention" and
     "the two functions v3 calls")."""
     n = (ctx + page - 1) // page
     pages = np.asarray(block_table_row[:n], dtype=np.int64)
-    g = cache[pages]  # [n, page, H, d]
+    g = cache[pages]  # [n, page, ...]
     return g.reshape(n * page, *cache.shape[2:])[:ctx]
 
 
@@ -169,9 +169,10 @@ def attention_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale
     heads = list(range(H)) if heads is None else list(heads)
     for b in seqs:
         ctx = int(context_lens[b])
-        kb = gather_paged(k_cache, block_table[b], ctx, page)
-        vb = gather_paged(v_cache, block_table[b], ctx, page)
         for h in heads:
-            ob, lb = attention_rows(q[b, h][None, :], kb[:, h], vb[:, h], scale, False)
+            # gather one head at a time: [ctx, d] instead of [ctx, H, d]
+            kb = gather_paged(k_cache[:, :, h], block_table[b], ctx, page)
+            vb = gather_paged(v_cache[:, :, h], block_table[b], ctx, page)
+            ob, lb = attention_rows(q[b, h][None, :], kb, vb, scale, False)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return o, lse
