@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fwd", "varlen", "decode"], default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -198,6 +200,14 @@ def main() -> int:
                          "frac": by5 / t5 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by5,
                          "note": "split kernel + combine kernel, both inside the timed launch"}
     res["wall_s_timed"] = wall
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 512 << 20
     if not args.no_cpu_baseline and "fwd" in ms:
         res["cpu_baseline"] = cpu_baseline(w3)
     print(json.dumps(res), flush=True)
