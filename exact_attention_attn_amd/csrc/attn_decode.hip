@@ -68,8 +68,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   constexpr int LPT = C::LPT, TPI = C::TPI, NI = C::NI;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y * 4 + wave;
+  const int h = blockIdx.x * 4 + wave;  // head groups of one (sequence, split) are adjacent
+  const int split = blockIdx.y;          // in dispatch order, so a page is read by all of
+                                         // them at about the same time
   const int b = blockIdx.z;
   if (h >= p.H) return;  // no barriers in this kernel: waves are independent
   const int ctx = p.context_lens[b];
@@ -242,7 +243,7 @@ template <int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   if (p.B <= 0 || p.H <= 0) return hipSuccess;
   if (p.max_splits > 0) {
-    dim3 grid((unsigned)p.max_splits, (unsigned)((p.H + 3) / 4), (unsigned)p.B);
+    dim3 grid((unsigned)((p.H + 3) / 4), (unsigned)p.max_splits, (unsigned)p.B);
     hipLaunchKernelGGL((decode_split_kernel<D>), grid, dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -49,18 +49,27 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Block index -> (row block, batch/sequence, head).  Blocks that share (b, h) are
-// H*B apart, so with round-robin dispatch over the 8 XCDs all row blocks of one head
-// land on the same XCD (and its L2) whenever H*B is a multiple of 8.  Causal launches
-// hand out the heaviest (last) row blocks first.
+// Block index -> (row block, batch/sequence, head).  Workgroups are dispatched
+// round-robin over the 8 XCDs (bid % 8), each with its own L2.  When the number of
+// (batch, head) pairs is a multiple of 8, XCD x takes pairs x, x+8, x+16, ... one after
+// the other, with all row blocks of a pair back to back, so the K/V of the pairs in
+// flight stay in that XCD's L2.  Causal launches take the heaviest (last) row block of
+// a pair first.
 template <bool CAUSAL>
 __device__ __forceinline__ void block_coords(const FwdParams& p, int& rb, int& b, int& h) {
-  const int nhb = p.H * p.B;
+  const int npairs = p.H * p.B;
   const int bid = blockIdx.x;
-  const int hb = bid % nhb;
-  const int rbi = bid / nhb;
-  b = hb / p.H;
-  h = hb - b * p.H;
+  int pair, rbi;
+  if ((npairs & 7) == 0) {
+    const int x = bid & 7, i = bid >> 3;
+    pair = x + 8 * (i / p.n_rb);
+    rbi = i - (i / p.n_rb) * p.n_rb;
+  } else {
+    pair = bid % npairs;
+    rbi = bid / npairs;
+  }
+  b = pair / p.H;
+  h = pair - b * p.H;
   rb = CAUSAL ? (p.n_rb - 1 - rbi) : rbi;
 }
 

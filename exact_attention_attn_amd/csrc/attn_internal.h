@@ -59,7 +59,10 @@ hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
 constexpr int kFwdBM = 128;
 // Row-block height of the fp32 forward kernel.
 constexpr int kFwdF32BM = 64;
-// Tokens per decode split.
-constexpr int kDecodeSplit = 512;
+// Tokens per decode split (a multiple of 16).
+#ifndef ATTN_DECODE_SPLIT
+#define ATTN_DECODE_SPLIT 512
+#endif
+constexpr int kDecodeSplit = ATTN_DECODE_SPLIT;
 
 }  // namespace attn
