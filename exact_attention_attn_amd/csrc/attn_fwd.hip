@@ -19,11 +19,12 @@
 //    the contraction follows the accumulator's layout, and V^T is read from LDS in
 //    that same order.  The O^T accumulator again gives each lane one query row, so
 //    the per-row rescale by exp(m_old - m_new) is a per-lane scalar multiply.
-//  * K tile: LDS row-major [key][d] (+16 B pad per row).  V tile: stored transposed
-//    [d][key] (+8 B pad) so that each lane reads 4 consecutive keys of one column with
-//    one 8-byte LDS read; the transpose happens while staging (dword global loads of
-//    whole V rows, byte permutes, 8-byte LDS stores).
-//  * The next K/V tile is fetched into registers while the current one is computed.
+//  * K and V tiles go global -> LDS with direct-to-LDS buffer loads (no VGPR staging),
+//    double-buffered; rows past the sequence end read as zero (buffer bounds) and are
+//    masked.  K tile: [key][16-byte chunk], chunk index XOR-swizzled by key so the
+//    MFMA operand reads hit distinct banks.  V tile: [32-column block][key][64 B]; the
+//    V^T operand comes from two LDS transposing reads (ds_read_b64_tr_b16), each
+//    covering 256 contiguous bytes.
 //  * Scores are kept in base-2 units: p = exp2(s * scale*log2(e) - m2), using the
 //    hardware exp2.
 //
