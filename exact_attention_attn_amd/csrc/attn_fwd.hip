@@ -32,6 +32,8 @@
 // recurrence: 4 lanes per query row, K/V tiles broadcast from LDS.
 #include "attn_internal.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
@@ -42,7 +44,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int BN = 64;  // keys per tile
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -114,39 +115,66 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // the result is the same function.  Most tiles then skip the O^T rescale.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFFll ? 0x7FFFFFFF : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw (unstrided) 16-byte loads of `bytes` bytes from `base`; reads
+// past the end return zero.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ u32x4s buffer_rsrc(const void* base, int64_t bytes) {
+  // bytes > 0 here; clamp with 32-bit compares (the scalar unit has no 64-bit ordered compare)
+  const unsigned hi = (unsigned)((uint64_t)bytes >> 32), lo = (unsigned)bytes;
+  const unsigned nrec = (hi != 0u || lo > 0x7FFFFFFFu) ? 0x7FFFFFFFu : lo;
+  const uint64_t a = (uint64_t)base;
+  u32x4s r;
+  r.x = (unsigned)a;
+  r.y = (unsigned)(a >> 32) & 0xFFFFu;
+  r.z = nrec;
+  r.w = 0x00020000u;
+  return r;
 }
 
-// 16-byte direct-to-LDS load per lane: lane i's data lands at lds + 16 i.  Kept out of
-// lambdas: the host pass would otherwise drop the kernel's launch stub.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
+// 16-byte direct-to-LDS load per lane: lane i's data lands at lds + 16 i.  Issued as
+// inline asm so the compiler does not see an asynchronous LDS write: it would otherwise
+// make every later LDS read wait for all outstanding loads, which serialises the
+// prefetch.  Completion is tracked explicitly (s_waitcnt vmcnt(0) before the barrier that
+// publishes a buffer).
+__device__ __forceinline__ void dma16(u32x4s r, const uint8_t* lds, int voffset) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)lds);
+  // The compiler's hazard recognizer does not look inside inline asm, so the wait states
+  // the load needs are spelled out: one after the SALU write of M0, and five after a
+  // VALU write of an SGPR it reads (v_readfirstlane of the descriptor or of M0's value).
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voffset), "s"(r)
+               : "memory", "m0");
 }
 
-template <int D, int NW, bool CAUSAL, bool VARLEN>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_bf16_kernel(const FwdParams p) {
+template <int D, int NW, int BN, bool CAUSAL, bool VARLEN>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ATTN_FWD_WPE, ATTN_FWD_WPE))) fwd_bf16_kernel(const FwdParams p) {
   constexpr int BM = 32 * NW;       // query rows per workgroup
-  constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
+  constexpr int NS = BN / 32;       // 32-key blocks per key tile
+  constexpr int NP = BN / 16;       // 16-key groups per key tile (B operands of O^T += V^T P^T)
   constexpr int DT = D / 16;        // k-steps of the S^T contraction
   constexpr int DB = D / 32;        // 32-column blocks of O^T
   constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int VBLK = BN * 64;             // bytes of one 32-column block of a V tile
   constexpr int NBLK = TILE_BYTES / 1024;   // 1 KiB direct-to-LDS blocks per K (or V) tile
   constexpr int BPW = NBLK / NW;            // blocks per wavefront
   static_assert(BPW * NW == NBLK, "tile split");
-  // LDS: two buffers, each [K tile | V tile]
-  //   K tile: [64 keys][CPR chunks], chunk c of key r stored at chunk c ^ (r % CPR)
-  //   V tile: [DB blocks][64 keys][4 chunks]  (32 columns of one key = 64 B)
-  // Two separate LDS objects (not one array indexed by parity): the compiler can then
-  // tell that reads of the current buffer do not alias the in-flight DMA into the other
-  // one, and does not stall them on the prefetch.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[2 * TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[2 * TILE_BYTES];
+  // LDS: K and V tiles, each double-buffered.  K runs one tile ahead of V: while
+  // tile j's V feeds P_j V_j, tile j+1's K feeds S_{j+1} = K_{j+1} Q^T.
+  //   K tile: in MFMA operand order, [DT k-steps][NS key blocks][2 halves][32 keys][16 B]:
+  //           the A operand of k-step t, key block c is the 1 KiB at (t * NS + c) * 1024,
+  //           lane i's 16 bytes at lane offset 16 i (no address arithmetic, no conflicts)
+  //   V tile: [DB blocks][BN keys][4 chunks]  (32 columns of one key = 64 B)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];  // K0 K1 V0 V1
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const kbuf1 = smem + TILE_BYTES;
+  uint8_t* const vbuf0 = smem + 2 * TILE_BYTES;
+  uint8_t* const vbuf1 = smem + 3 * TILE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS DMA bases stay in SGPRs
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -162,6 +190,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   int kend = Lk;
   if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
   const int ntiles = (kend + BN - 1) / BN;
+  // tiles [0, nfull) need no mask for any row of this workgroup
+  int nfull = Lk / BN;
+  if (CAUSAL) nfull = min(nfull, max(0, (row0 + shift + 1) / BN));
 
   const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + qoff;
   const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + koff;
@@ -179,35 +210,55 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
     qreg[t] = as_bf16x8(u);
   }
 
-  // per-lane byte offsets of this wavefront's direct-to-LDS loads (relative to the tile's first key)
-  int kvoff[BPW], vvoff[BPW];
+  // Per-lane source rows and in-row byte offsets of this wavefront's direct-to-LDS loads.
+  // In the last tile, rows past the sequence end are clamped to its last row: the
+  // direct-to-LDS path does not reliably write zeros for out-of-range rows, and stale LDS
+  // data times a zero probability could be NaN.  Clamped keys are masked to -inf.
+  int kkey[BPW], kcol[BPW], vkey[BPW], vcol[BPW], kdoff[BPW], vdoff[BPW];
+  const int krow_bytes = (int)ksn * 2, vrow_bytes = (int)vsn * 2;
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int bi = wave * BPW + i;
-    {  // K block bi: keys (1024 / (2D)) * bi + lane / CPR, stored chunk lane % CPR
-      constexpr int KPB = 1024 / (2 * D);
-      const int key = KPB * bi + lane / CPR;
-      const int logical = (lane % CPR) ^ (key % CPR);
-      kvoff[i] = key * (int)ksn * 2 + logical * 16;
+    {  // K block bi = (k-step t, key block c): key 32c + lane % 32, chunk 2t + lane / 32
+      const int t = bi / NS, c = bi % NS;
+      kkey[i] = 32 * c + (lane & 31);
+      kcol[i] = (2 * t + (lane >> 5)) * 16;
     }
-    {  // V block bi: column block bi / 4, keys 16 * (bi % 4) + lane / 4, chunk lane % 4
-      const int db = bi / 4, key = 16 * (bi % 4) + lane / 4;
-      vvoff[i] = key * (int)vsn * 2 + (32 * db + 8 * (lane % 4)) * 2;
+    {  // V block bi: column block bi / (BN / 16), keys 16 * (bi % (BN / 16)) + lane / 4, chunk lane % 4
+      const int db = bi / (BN / 16);
+      vkey[i] = 16 * (bi % (BN / 16)) + lane / 4;
+      vcol[i] = (32 * db + 8 * (lane % 4)) * 2;
     }
+    kdoff[i] = kkey[i] * krow_bytes + kcol[i];
+    vdoff[i] = vkey[i] * vrow_bytes + vcol[i];
   }
 
-  auto issue_tile = [&](int j, uint8_t* kb) {
+  auto issue_k = [&](int j, uint8_t* kb) {
     const int kt0 = j * BN;
-    const int64_t krem = ((int64_t)(Lk - kt0 - 1) * ksn + D) * 2;  // bytes of valid keys from kt0 on
-    const int64_t vrem = ((int64_t)(Lk - kt0 - 1) * vsn + D) * 2;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (int64_t)kt0 * ksn, krem);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (int64_t)kt0 * vsn, vrem);
-    uint8_t* vb = kb + TILE_BYTES;
+    const int last = Lk - kt0 - 1;  // last valid row of this tile (>= 0)
+    const int64_t krem = ((int64_t)last * ksn + D) * 2;  // bytes of valid keys from kt0 on
+    const u32x4s kr = buffer_rsrc(Kg + (int64_t)kt0 * ksn, krem);
+    if (last >= BN - 1) {
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int bi = wave * BPW + i;
-      dma16(kr, kb + bi * 1024, kvoff[i]);
-      dma16(vr, vb + bi * 1024, vvoff[i]);
+      for (int i = 0; i < BPW; ++i) dma16(kr, kb + (wave * BPW + i) * 1024, kdoff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        dma16(kr, kb + (wave * BPW + i) * 1024, min(kkey[i], last) * krow_bytes + kcol[i]);
+    }
+  };
+  auto issue_v = [&](int j, uint8_t* vb) {
+    const int kt0 = j * BN;
+    const int last = Lk - kt0 - 1;
+    const int64_t vrem = ((int64_t)last * vsn + D) * 2;
+    const u32x4s vr = buffer_rsrc(Vg + (int64_t)kt0 * vsn, vrem);
+    if (last >= BN - 1) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) dma16(vr, vb + (wave * BPW + i) * 1024, vdoff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        dma16(vr, vb + (wave * BPW + i) * 1024, min(vkey[i], last) * vrow_bytes + vcol[i]);
     }
   };
 
@@ -218,98 +269,162 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2,
   float l = 0.f;
   const float c2 = p.scale_log2;
 
-  // LDS read offsets (bytes within a buffer)
-  const int ksw = col % CPR;
-  const int kread = col * (2 * D);                              // key = 32c + col, + c * 64 * D
-  const int vread = TILE_BYTES + (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  // LDS read offsets
+  const int kread = lane * 16;
+  const int vread = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-  auto compute_tile = [&](int j, const uint8_t* kb) {
-    const int kt0 = j * BN;
-    if (CAUSAL && kt0 > wrow0 + 31 + shift) return;  // whole tile above this wave's rows
-    // ---- S^T = K Q^T
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const int off = kread + (((2 * t + half) ^ ksw) * 16);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 a = *(const lds_u32x4*)(kb + off + c * 64 * D);
-        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[t], sacc[c], 0, 0, 0);
-      }
-    }
+  // K operand of S^T = K Q^T for k-step t and key block c (16 bytes per lane)
+  auto kop = [&](const uint8_t* kb, int t, int c) -> u32x4 {
+    return *(const lds_u32x4*)(kb + kread + (t * NS + c) * 1024);
+  };
+  // V^T operand of O^T += V^T P^T for column block db and key group t4 (two transposing reads)
+  auto vop = [&](const uint8_t* vb, int db, int t4) -> bf16x8 {
+    const uint8_t* vp = vb + vread + db * VBLK + t4 * 1024;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // tail keys and (causal) keys above the diagonal -> -inf; element (c, v) of the tile
+  auto mask1 = [&](int kt0, float x, int c, int v) -> float {
+    const int key = kt0 + 32 * c + 8 * (v >> 2) + 4 * half + (v & 3);
+    const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
+    return ok ? x : kNegInf;
+  };
+  auto finish_max = [&](float mx, float& mnew, bool& grow) {
+    mx = fmaxf(mx, xor32(mx)) * c2;
+    grow = mx > m2 + kRescaleSlack;  // also true on a row's first admissible key
+    mnew = grow ? mx : m2;
+  };
 
-    // ---- masking: tail keys and (causal) keys above the diagonal
-    const bool need_mask = (kt0 + BN > Lk) || (CAUSAL && kt0 + BN - 1 > wrow0 + shift);
-    if (need_mask) {
+  if (ntiles > 0) {
+    // prologue: K0, V0, K1 in flight; S_0 and its row max
+    issue_k(0, kbuf0);
+    issue_v(0, vbuf0);
+    if (ntiles > 1) issue_k(1, kbuf1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sA[NS], sB[NS];  // S of the current and the next tile, alternating roles
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NS; ++c) sA[c] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
+        sA[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop(kbuf0, t, c)), qreg[t], sA[c], 0, 0, 0);
+    float mnew;
+    bool grow;
+    {
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < NS; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = kt0 + 32 * c + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
-          if (!ok) sacc[c][v] = kNegInf;
+          if (nfull < 1) sA[c][v] = mask1(0, sA[c][v], c, v);
+          mx = fmaxf(mx, sA[c][v]);
         }
+      finish_max(mx, mnew, grow);
     }
 
-    // ---- online softmax with deferred rescale
-    float mx = kNegInf;
+    // Step j, software-pipelined inside one wavefront (MFMA and VALU work of the same
+    // wavefront overlap; separate wavefronts on a SIMD barely do):
+    //   phase 1: S_{j+1} = K_{j+1} Q^T (NS MFMAs per k-step) interleaved with the
+    //            exponentials, row sums and bf16 packing of tile j;
+    //   phase 2: O^T += V_j^T P_j^T (1 MFMA per chunk) interleaved with masking and the
+    //            row max of tile j+1.
+    // Scheduling barriers keep each chunk's MFMAs next to its VALU share.  Tiles that
+    // cross the diagonal or the sequence end are masked after phase 2 (a few per row
+    // block).  The last step's S_{j+1} is computed on a stale buffer and discarded.
+    // Step j: see the comment above.  Buffers: K_j in kbuf[j % 2], V_j in vbuf[j % 2].
+    auto step = [&](int j, const uint8_t* kcur, uint8_t* kdma, const uint8_t* vcur, uint8_t* vdma,
+                    f32x16* s_cur, f32x16* sn) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K_{j+1}, V_j landed
+      __syncthreads();                                   // ... and every wave's
+      // the first two k-steps' K operands are requested before anything else
+      constexpr int KPF = 2;  // k-steps of K operands in flight
+      u32x4 a[KPF][NS];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int u = 0; u < KPF; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][v]);
-    mx = fmaxf(mx, xor32(mx)) * c2;
-    const bool grow = mx > m2 + kRescaleSlack;  // also true on a row's first admissible key
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mnew = grow ? mx : m2;
-      const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
-      l *= alpha;
+        for (int c = 0; c < NS; ++c) a[u][c] = kop(kcur, u, c);
+      if (j + 2 < ntiles) issue_k(j + 2, kdma);
+      if (j + 1 < ntiles) issue_v(j + 1, vdma);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {      // deferred rescale (rare)
+        const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
+        l *= alpha;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      m2 = mnew;
+        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+        m2 = mnew;
+      }
+      const float muse = (m2 == kNegInf) ? 0.f : m2;  // no admissible key yet: p = 0
+
+      // phase 1
+      constexpr int EPC = 16 * NS / DT;  // exponentials per k-step
+#pragma unroll
+      for (int c = 0; c < NS; ++c) sn[c] = f32x16{};
+      bf16x8 pb[NP];
+      float rs = 0.f;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        u32x4 n[NS];
+#pragma unroll
+        for (int c = 0; c < NS; ++c) n[c] = (t + KPF < DT) ? kop(kcur, t + KPF, c) : a[t % KPF][c];
+#pragma unroll
+        for (int c = 0; c < NS; ++c)
+          sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[t % KPF][c]), qreg[t], sn[c], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int idx = t * EPC + e;  // 0..16*NS-1: key group idx/8, element idx%8
+          const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
+          rs += pv;
+          pb[idx >> 3][idx & 7] = (__bf16)pv;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NS; ++c) a[t % KPF][c] = n[c];
+      }
+      l += rs + xor32(rs);
+
+      // phase 2
+      constexpr int NCH = NP * DB;          // O^T MFMAs per tile
+      constexpr int SPC = 16 * NS / NCH;    // tile j+1 scores handled per chunk
+      const int kt1 = (j + 1) * BN;
+      float mx = kNegInf;
+      bf16x8 va = vop(vcur, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int db = k / NP, t4 = k % NP;
+        bf16x8 vn = va;
+        if (k + 1 < NCH) vn = vop(vcur, (k + 1) / NP, (k + 1) % NP);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t4], oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < SPC; ++e) {
+          const int idx = k * SPC + e;
+          const int c = idx >> 4, v = idx & 15;
+          mx = fmaxf(mx, sn[c][v]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        va = vn;
+      }
+      if (j + 1 >= nfull) {  // tile j+1 crosses the diagonal or the tail: mask, redo the max
+        mx = kNegInf;
+#pragma unroll
+        for (int c = 0; c < NS; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            sn[c][v] = mask1(kt1, sn[c][v], c, v);
+            mx = fmaxf(mx, sn[c][v]);
+          }
+      }
+      finish_max(mx, mnew, grow);
+    };
+    // unrolled by two so every buffer address is a compile-time offset and S alternates
+    // between sA and sB without copies; an odd last step runs after the loop
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+      step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
+      step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, sB, sA);
     }
-    const float muse = (m2 == kNegInf) ? 0.f : m2;  // row without admissible key so far: p = 0
-    float rs = 0.f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = exp2_fast(__builtin_fmaf(sacc[c][v], c2, -muse));
-        sacc[c][v] = pv;
-        rs += pv;
-      }
-    l += rs + xor32(rs);
-
-    // ---- P^T as the B operand (bf16, round to nearest even)
-    bf16x8 pb[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)sacc[t >> 1][8 * (t & 1) + e];
-
-    // ---- O^T += V^T P^T; V^T operand through the LDS transposing read
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint8_t* vp = kb + vread + db * 4096 + t * 1024;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], oacc[db], 0, 0, 0);
-      }
-  };
-
-  auto step = [&](int j, uint8_t* cur, uint8_t* nxt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA into `cur` landed
-    __syncthreads();                                   // ... and every wave's; `nxt` is free
-    if (j + 1 < ntiles) issue_tile(j + 1, nxt);
-    compute_tile(j, cur);
-  };
-
-  if (ntiles > 0) issue_tile(0, smem0);
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, smem0, smem1);
-    if (j + 1 < ntiles) step(j + 1, smem1, smem0);
+    if (j < ntiles) step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
   }
 
   // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
@@ -435,10 +550,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bf16_t(const FwdParams& p, hipStream_t s) {
-  constexpr int NW = kFwdBM / 32;
+  constexpr int NW = kFwdNW;
   const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
   if (nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -55,8 +55,22 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, 
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
 
+// Wavefronts per workgroup of the bf16 forward kernel; each owns 32 query rows.
+#ifndef ATTN_FWD_NW
+#define ATTN_FWD_NW 4
+#endif
+constexpr int kFwdNW = ATTN_FWD_NW;
+// Wavefronts per SIMD the bf16 forward kernel is compiled for (register budget).
+#ifndef ATTN_FWD_WPE
+#define ATTN_FWD_WPE 2
+#endif
+// Keys per K/V tile of the bf16 forward kernel (32 or 64).
+#ifndef ATTN_FWD_BN
+#define ATTN_FWD_BN 64
+#endif
+constexpr int kFwdBN = ATTN_FWD_BN;
 // Row-block height of the bf16 forward kernel (query rows per workgroup).
-constexpr int kFwdBM = 128;
+constexpr int kFwdBM = 32 * kFwdNW;
 // Row-block height of the fp32 forward kernel.
 constexpr int kFwdF32BM = 64;
 // Tokens per decode split (a multiple of 16).

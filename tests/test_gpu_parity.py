@@ -156,6 +156,43 @@ def test_dense_ragged_fp32(A, N, Nk, causal, d):
     assert_close("lse", lse, rl, TOL_F32)
 
 
+@pytest.mark.parametrize("N,Nk,causal,d", [(100, 77, False, 64), (100, 77, True, 128), (33, 200, True, 64),
+                                           (1, 1, False, 128), (130, 300, False, 128)])
+def test_dense_tail_poison(A, N, Nk, causal, d):
+    """K/V rows past Nk hold NaN in the same allocation (the tensors passed are views of
+    larger buffers): no such row may reach the output."""
+    import torch
+    w = synth.dense(1, 2, N, d, "bf16", causal, seed=N + Nk + d, Nk=Nk)
+    q = dev(w.q)
+    pad = 64
+    kb = torch.full((1, 2, Nk + pad, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((1, 2, Nk + pad, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb[:, :, :Nk] = dev(w.k)
+    vb[:, :, :Nk] = dev(w.v)
+    o, lse = A.attn_fwd(q, kb[:, :, :Nk], vb[:, :, :Nk], scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, causal)
+    assert_close("O", host(o), ro, TOL_BF16_O)
+    assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
+def test_varlen_tail_poison(A):
+    """Tokens after the last sequence are NaN: reading past a sequence's keys shows up."""
+    import torch
+    w = synth.varlen(H=2, d=128, causal=False, seed=11, lens=[70, 5, 33])
+    tk = int(w.cu_k[-1])
+    kb = torch.full((tk + 64, 2, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((tk + 64, 2, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb[:tk] = dev(w.k)
+    vb[:tk] = dev(w.v)
+    o, lse = A.attn_fwd_varlen(dev(w.q), kb[:tk], vb[:tk], dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=False)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, False)
+    assert_close("O", host(o), ro, TOL_BF16_O)
+    assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
 def test_dense_strided_layout(A):
     """[B, N, H, d] memory order passed through the stride arguments."""
     w = synth.dense(2, 4, 190, 128, "bf16", True, seed=5)
