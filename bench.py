@@ -33,6 +33,13 @@ METRIC = "attn fwd TFLOP/s + %MFMA peak (N=8192,d=128 bf16); paged decode HBM GB
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
+# HBM bytes per launch of the dense forward kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (KiB per dispatch), scaled by what the same counters read for a 512 MiB device copy
+# (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
+# kernel source they were taken on (sha256 prefix); reported as null otherwise.
+FWD_COUNTERS = {"source_sha256_16": "7ce42f6ccafc3fb0", "fetch_kib": 107071.0, "write_kib": 66560.0,
+                "fetch_scale": 2.0, "write_scale": 1.0}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -57,6 +64,19 @@ def decode_bytes(ctx, B: int, H: int, d: int, page: int) -> int:
 
 def fwd_bytes(B: int, H: int, N: int, d: int) -> int:
     return B * H * (4 * N * d * 2 + 4 * N)
+
+
+def fwd_traffic_bytes():
+    """Counter-measured HBM bytes per dense forward launch, or None if the kernel source
+    changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "exact_attention_attn_amd", "csrc", "attn_fwd.hip")
+    with open(src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    c = FWD_COUNTERS
+    if h != c["source_sha256_16"]:
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
@@ -183,7 +203,7 @@ def main() -> int:
         ach = fl3 / t3 / 1e12
         res["value"] = ach
         res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": fwd_traffic_bytes(),
                            "kernel": "fwd_bf16_kernel<128,4,causal>", "flops_per_launch": fl3,
                            "algorithmic_bytes_per_launch": fwd_bytes(1, 32, 8192, 128)}
     else:
