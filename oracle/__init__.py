@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
     attention_varlen,
     attention_decode_paged,
     gather_paged,
+    kv_head,
     probabilities,
 )
 from .online import online_attention  # noqa: F401

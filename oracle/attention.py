@@ -16,6 +16,12 @@ Readings where the pages are silent (each is listed in the design doc):
 * lse = m + ln(l), natural log, in units of the scaled score;
 * keys past a sequence's end simply do not exist (never a zero-filled key).
 
+Grouped-query attention ("From standard Attention to FlashAttention and paged
+execution", section "GQA: handled natively by the kernel, K/V not expanded"): K/V
+hold H_kv heads, H_kv divides H, and query head h uses KV head h // (H // H_kv) --
+the head order the page's explicit expansion of each KV head into H // H_kv copies
+produces.
+
 Rows are independent (dlog.com.cn, section 2.1), so computing a chunk of rows at
 a time is exact; it only bounds memory.
 """
@@ -92,18 +98,28 @@ def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
         return np.where(l > 0, p / np.where(l > 0, l, 1.0), 0.0)
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """KV head read by query head h under grouped-query attention (H_kv divides H)."""
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError(f"H_kv={H_kv} must divide H={H}")
+    return h // (H // H_kv)
+
+
 def attention_dense(q, k, v, scale: float, causal: bool = False, heads=None, rows=None):
-    """Dense batched attention, Q [B, H, N, d], K/V [B, H, Nk, d] (the [B, H, N, d]
-    layout of the pages' Triton kernels).  Returns O [B, H, N, d] and lse [B, H, N]
-    float64.  ``heads`` restricts to a list of (b, h) pairs (the other entries stay
-    NaN); ``rows`` restricts the query rows (same for each head)."""
+    """Dense batched attention, Q [B, H, N, d], K/V [B, H_kv, Nk, d] (the [B, H, N, d]
+    layout of the pages' Triton kernels; H_kv = H unless grouped-query).  Returns
+    O [B, H, N, d] and lse [B, H, N] float64.  ``heads`` restricts to a list of (b, h)
+    pairs (the other entries stay NaN); ``rows`` restricts the query rows (same for
+    each head)."""
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     dv = v.shape[3]
     o = np.full((B, H, N, dv), np.nan)
     lse = np.full((B, H, N), np.nan)
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     for b, h in pairs:
-        ob, lb = attention_rows(q[b, h], k[b, h], v[b, h], scale, causal, rows=rows)
+        hk = kv_head(h, H, H_kv)
+        ob, lb = attention_rows(q[b, h], k[b, hk], v[b, hk], scale, causal, rows=rows)
         if rows is None:
             o[b, h], lse[b, h] = ob, lb
         else:
@@ -118,9 +134,11 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, se
     Q [total_q, H, d] and K/V [total_k, H, d]; sequence s owns rows
     [cu_q[s], cu_q[s+1]) of Q and [cu_k[s], cu_k[s+1]) of K/V (the page's example
     cu_seqlens [0, 3, 7] means ranges [0,3) and [3,7)).  Each sequence is attended
-    independently.  Returns O [total_q, H, d], lse [total_q, H] (NaN where not
-    computed when restricted by ``seqs``/``heads``/``rows_per_seq``)."""
+    independently.  K/V may hold fewer (grouped-query) heads.  Returns
+    O [total_q, H, d], lse [total_q, H] (NaN where not computed when restricted by
+    ``seqs``/``heads``/``rows_per_seq``)."""
     tq, H, d = q.shape
+    H_kv = k.shape[1]
     dv = v.shape[2]
     o = np.full((tq, H, dv), np.nan)
     lse = np.full((tq, H), np.nan)
@@ -134,7 +152,8 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, se
         if rows_per_seq is not None:
             rows = np.asarray(rows_per_seq(s, q1 - q0), dtype=np.int64)
         for h in heads:
-            ob, lb = attention_rows(q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], scale, causal,
+            hk = kv_head(h, H, H_kv)
+            ob, lb = attention_rows(q[q0:q1, h], k[k0:k1, hk], v[k0:k1, hk], scale, causal,
                                     rows=rows)
             if rows is None:
                 o[q0:q1, h], lse[q0:q1, h] = ob, lb
@@ -159,8 +178,10 @@ def attention_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale
     """Decode over a paged KV cache: sequence b's single query q[b] [H, d] attends
     its context_lens[b] cached tokens, gathered through block_table[b] (page size =
     k_cache.shape[1]).  With one query token, bottom-right causal and non-causal
-    coincide.  Returns O [B, H, d], lse [B, H] (NaN where not computed)."""
+    coincide.  The pools hold H_kv (grouped-query) heads: [pages, page, H_kv, d].
+    Returns O [B, H, d], lse [B, H] (NaN where not computed)."""
     B, H, d = q.shape
+    H_kv = k_cache.shape[2]
     page = k_cache.shape[1]
     dv = v_cache.shape[3]
     o = np.full((B, H, dv), np.nan)
@@ -171,8 +192,9 @@ def attention_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale
         ctx = int(context_lens[b])
         for h in heads:
             # gather one head at a time: [ctx, d] instead of [ctx, H, d]
-            kb = gather_paged(k_cache[:, :, h], block_table[b], ctx, page)
-            vb = gather_paged(v_cache[:, :, h], block_table[b], ctx, page)
+            hk = kv_head(h, H, H_kv)
+            kb = gather_paged(k_cache[:, :, hk], block_table[b], ctx, page)
+            vb = gather_paged(v_cache[:, :, hk], block_table[b], ctx, page)
             ob, lb = attention_rows(q[b, h][None, :], kb, vb, scale, False)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return o, lse

@@ -359,3 +359,76 @@ def test_optional_sdpa_crosscheck():
         t = torch.nn.functional.scaled_dot_product_attention(
             torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=0.25)
         assert np.abs(o - t.numpy()).max() < 1e-12
+
+
+# ----------------------------------------------------------------- grouped-query attention
+
+def _expand_kv(x, groups, axis):
+    """The page's explicit GQA expansion (section "GQA: handled natively by the kernel"):
+    each KV head repeated `groups` times along the head axis, KV head-major."""
+    shp = list(x.shape)
+    y = np.expand_dims(x, axis + 1)
+    y = np.broadcast_to(y, shp[:axis + 1] + [groups] + shp[axis + 1:])
+    return y.reshape(shp[:axis] + [shp[axis] * groups] + shp[axis + 1:])
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (8, 2), (6, 3), (4, 1), (4, 4)])
+def test_gqa_dense_equals_expanded_kv(H, Hkv):
+    r = rng(20 + H + Hkv)
+    q = r.normal(size=(2, H, 9, 5))
+    k, v = r.normal(size=(2, Hkv, 11, 5)), r.normal(size=(2, Hkv, 11, 5))
+    for causal in (False, True):
+        o, l = oracle.attention_dense(q, k, v, 0.4, causal)
+        g = H // Hkv
+        oe, le = oracle.attention_dense(q, _expand_kv(k, g, 1), _expand_kv(v, g, 1), 0.4, causal)
+        assert np.array_equal(o, oe) and np.array_equal(l, le)
+
+
+def test_gqa_head_mapping_brute_force():
+    """Query head h must read KV head h // (H / H_kv): heads 0,1 -> 0 and 2,3 -> 1 here
+    (a modulo mapping h % H_kv would pair heads 0,2 and 1,3 and fails)."""
+    r = rng(30)
+    q = r.normal(size=(1, 4, 3, 2))
+    k, v = r.normal(size=(1, 2, 4, 2)), r.normal(size=(1, 2, 4, 2))
+    o, l = oracle.attention_dense(q, k, v, 0.8, False)
+    for h, hk in ((0, 0), (1, 0), (2, 1), (3, 1)):
+        ob, lb = _brute(q[0, h].tolist(), k[0, hk].tolist(), v[0, hk].tolist(), 0.8, False)
+        assert np.abs(o[0, h] - ob).max() < TIGHT and np.abs(l[0, h] - lb).max() < TIGHT
+
+
+def test_gqa_rejects_non_dividing_heads():
+    r = rng(31)
+    with pytest.raises(ValueError):
+        oracle.attention_dense(r.normal(size=(1, 4, 2, 2)), r.normal(size=(1, 3, 2, 2)),
+                               r.normal(size=(1, 3, 2, 2)), 1.0)
+
+
+def test_gqa_varlen_equals_expanded_kv():
+    r = rng(32)
+    cu = np.array([0, 3, 7, 12], dtype=np.int32)
+    q = r.normal(size=(12, 8, 4))
+    k, v = r.normal(size=(12, 2, 4)), r.normal(size=(12, 2, 4))
+    for causal in (False, True):
+        o, l = oracle.attention_varlen(q, k, v, cu, cu, 0.5, causal)
+        oe, le = oracle.attention_varlen(q, _expand_kv(k, 4, 1), _expand_kv(v, 4, 1), cu, cu, 0.5, causal)
+        assert np.array_equal(o, oe) and np.array_equal(l, le)
+
+
+def test_gqa_paged_decode_brute_force():
+    r = rng(33)
+    page, H, Hkv, d = 4, 4, 2, 3
+    ctx = np.array([5, 9], dtype=np.int32)
+    P = 5
+    bt = np.array([[3, 0, 5], [1, 4, 2]], dtype=np.int32)   # page 5 = poison, never read
+    kc, vc = r.normal(size=(P + 1, page, Hkv, d)), r.normal(size=(P + 1, page, Hkv, d))
+    kc[P] = np.nan
+    vc[P] = np.nan
+    q = r.normal(size=(2, H, d))
+    o, l = oracle.attention_decode_paged(q, kc, vc, bt, ctx, 0.6)
+    for b, c in enumerate(ctx):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            ks = [kc[bt[b, t // page], t % page, hk].tolist() for t in range(c)]
+            vs = [vc[bt[b, t // page], t % page, hk].tolist() for t in range(c)]
+            ob, lb = _brute([q[b, h].tolist()], ks, vs, 0.6, False)
+            assert np.abs(o[b, h] - ob[0]).max() < TIGHT and abs(l[b, h] - lb[0]) < TIGHT
