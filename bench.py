@@ -6,6 +6,7 @@ One step = one call of each entry point on its workload, inputs resident in HBM:
   attn_fwd_varlen    16 sequences, lengths U[128,4096], H=32 d=128 bf16 causal
   attn_decode_paged  64 sequences, context U[512,8192], 16-token pages, H=32 d=128 bf16
                      (headline, HBM GB/s)
+  attn_decode_paged  the same lengths with 16 query heads on 8 KV heads (grouped-query)
 
 W untimed warm-up steps, then K timed steps; every kernel call is bracketed by HIP
 events on the stream it runs on.  Prints ONE JSON line.  `value` is the dense
@@ -55,11 +56,12 @@ def varlen_flops(lens, H: int, d: int) -> float:
     return float(np.sum(2.0 * d * H * L * (L + 1)))
 
 
-def decode_bytes(ctx, B: int, H: int, d: int, page: int) -> int:
-    """Ideal HBM traffic: each context token's K and V once, q read, O and lse written,
-    the used block-table entries and the context lengths."""
+def decode_bytes(ctx, B: int, H: int, d: int, page: int, H_kv: int | None = None) -> int:
+    """Ideal HBM traffic: each context token's K and V once (H_kv heads), q read, O and
+    lse written (H heads), the used block-table entries and the context lengths."""
+    H_kv = H if H_kv is None else H_kv
     c = np.asarray(ctx, dtype=np.int64)
-    return int(c.sum() * H * d * 2 * 2 + B * H * d * 2 * 2 + B * H * 4 + ((c + page - 1) // page).sum() * 4 + B * 4)
+    return int(c.sum() * H_kv * d * 2 * 2 + B * H * d * 2 * 2 + B * H * 4 + ((c + page - 1) // page).sum() * 4 + B * 4)
 
 
 def fwd_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -107,7 +109,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "varlen", "decode"], default=None,
+    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa"], default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
@@ -151,6 +153,16 @@ def main() -> int:
     w5.k_cache = w5.v_cache = None   # host copies no longer needed
     log(f"[bench] decode workload ready ({time.perf_counter() - t:.1f} s)")
 
+    w6 = synth.workload("gqa_decode")
+    q6, kc6, vc6 = dev(w6.q), dev(w6.k_cache), dev(w6.v_cache)
+    bt6, cl6 = dev(w6.block_table), dev(w6.context_lens)
+    maxctx6 = int(w6.context_lens.max())
+    ws6 = torch.empty(attn.attn_decode_paged_workspace_size(64, 16, 128, maxctx6, 16), dtype=torch.uint8, device="cuda")
+    o6 = torch.empty_like(q6)
+    l6 = torch.empty((64, 16), dtype=torch.float32, device="cuda")
+    w6.k_cache = w6.v_cache = None
+    log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
+
     def run_fwd():
         attn.attn_fwd(q3, k3, v3, scale=w3.scale, causal=True, out=o3, lse=l3)
 
@@ -160,7 +172,10 @@ def main() -> int:
     def run_decode():
         attn.attn_decode_paged(q5, kc5, vc5, bt5, cl5, maxctx5, scale=w5.scale, workspace=ws5, out=o5, lse=l5)
 
-    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode)]
+    def run_decode_gqa():
+        attn.attn_decode_paged(q6, kc6, vc6, bt6, cl6, maxctx6, scale=w6.scale, workspace=ws6, out=o6, lse=l6)
+
+    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa)]
     if args.only:
         parts = [p for p in parts if p[0] == args.only]
 
@@ -219,6 +234,13 @@ def main() -> int:
                          "ms": ms["decode"].mean(), "GB/s": by5 / t5 / 1e9, "peak": PEAK_HBM_GBS,
                          "frac": by5 / t5 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by5,
                          "note": "split kernel + combine kernel, both inside the timed launch"}
+    if "decode_gqa" in ms:
+        t6 = ms["decode_gqa"].mean() / 1e3
+        by6 = decode_bytes(w6.context_lens, 64, 16, 128, 16, H_kv=8)
+        res["decode_gqa"] = {"workload": "64 seqs ctx U[512,8192] (seed 0) 16-token pages H=16 H_kv=8 d=128 bf16",
+                             "ms": ms["decode_gqa"].mean(), "GB/s": by6 / t6 / 1e9, "peak": PEAK_HBM_GBS,
+                             "frac": by6 / t6 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by6,
+                             "note": "KV bytes counted once per KV head (grouped-query)"}
     res["wall_s_timed"] = wall
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")

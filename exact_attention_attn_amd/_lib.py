@@ -38,13 +38,13 @@ def load() -> ctypes.CDLL:
         raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_attention_attn_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64p, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_float, ctypes.c_size_t
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64p, i64p, i64p, i64p, f32, i32, vp]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64p, i64p, i64p, i64p, f32, i32, vp]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.attn_fwd_varlen.restype = i32
     lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_paged_workspace_size.restype = sz
-    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_decode_paged.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -95,15 +95,16 @@ def _check(rc: int, where: str):
 
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
              with_lse: bool = True, stream=None):
-    """Dense attention.  q [B, H, N, d], k/v [B, H, Nk, d] (bf16 or fp32, any strides
-    with a contiguous last dim).  Returns (o, lse) with o like q and lse float32
-    [B, H, N] (None when ``with_lse`` is false)."""
+    """Dense attention.  q [B, H, N, d], k/v [B, H_kv, Nk, d] (bf16 or fp32, any strides
+    with a contiguous last dim; H_kv divides H: grouped-query attention when smaller).
+    Returns (o, lse) with o like q and lse float32 [B, H, N] (None when ``with_lse``
+    is false)."""
     torch = _torch()
     lib = load()
     B, H, N, d = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
-        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -111,7 +112,7 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
     if with_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     rc = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if with_lse else None,
-                      B, H, N, Nk, d, _dtype_code(q), _strides3(q), _strides3(k), _strides3(v),
+                      B, H, Hkv, N, Nk, d, _dtype_code(q), _strides3(q), _strides3(k), _strides3(v),
                       _strides3(o), scale, int(bool(causal)), _stream(stream))
     _check(rc, "attn_fwd")
     return o, (lse if with_lse else None)
@@ -120,12 +121,15 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                     scale: float | None = None, causal: bool = False, out=None, lse=None,
                     with_lse: bool = True, stream=None):
-    """Packed variable-length attention.  q [total_q, H, d], k/v [total_k, H, d]
-    contiguous bf16; cu_seqlens_* int32 device tensors [num_seqs + 1].  Returns
-    (o [total_q, H, d], lse float32 [total_q, H])."""
+    """Packed variable-length attention.  q [total_q, H, d], k/v [total_k, H_kv, d]
+    contiguous bf16 (H_kv divides H); cu_seqlens_* int32 device tensors
+    [num_seqs + 1].  Returns (o [total_q, H, d], lse float32 [total_q, H])."""
     torch = _torch()
     lib = load()
     tq, H, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H_kv, d] matching q")
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("varlen tensors must be contiguous [tokens, H, d]")
@@ -140,7 +144,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         lse = torch.empty((tq, H), dtype=torch.float32, device=q.device)
     rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if with_lse else None,
                              _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q),
-                             int(max_seqlen_k), H, d, _dtype_code(q), scale, int(bool(causal)),
+                             int(max_seqlen_k), H, Hkv, d, _dtype_code(q), scale, int(bool(causal)),
                              _stream(stream))
     _check(rc, "attn_fwd_varlen")
     return o, (lse if with_lse else None)
@@ -153,14 +157,16 @@ def attn_decode_paged_workspace_size(B: int, H: int, d: int, max_context_len: in
 def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
                       scale: float | None = None, workspace=None, out=None, lse=None,
                       with_lse: bool = True, stream=None):
-    """Decode over a paged KV pool.  q [B, H, d]; k_cache/v_cache [num_pages, page, H, d]
-    bf16 contiguous; block_table int32 [B, max_pages]; context_lens int32 [B].
+    """Decode over a paged KV pool.  q [B, H, d]; k_cache/v_cache [num_pages, page, H_kv, d]
+    bf16 contiguous (H_kv divides H); block_table int32 [B, max_pages]; context_lens int32 [B].
     ``workspace`` (uint8 device tensor) is allocated here when not given.  Returns
     (o [B, H, d], lse float32 [B, H])."""
     torch = _torch()
     lib = load()
     B, H, d = q.shape
-    num_pages, page = k_cache.shape[0], k_cache.shape[1]
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page, H_kv, d] matching q")
     for t in (q, k_cache, v_cache, block_table, context_lens):
         if not t.is_contiguous():
             raise ValueError("decode tensors must be contiguous")
@@ -175,7 +181,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     rc = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse) if with_lse else None,
                                _ptr(block_table), block_table.shape[1], _ptr(context_lens), B, num_pages,
-                               page, H, d, int(max_context_len), scale, _ptr(workspace),
+                               page, H, Hkv, d, int(max_context_len), scale, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "attn_decode_paged")
     return o, (lse if with_lse else None)

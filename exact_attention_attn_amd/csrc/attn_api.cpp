@@ -50,11 +50,14 @@ inline int check_launch(hipError_t e) {
 
 inline int n_splits(int max_ctx) { return (max_ctx + attn::kDecodeSplit - 1) / attn::kDecodeSplit; }
 
+// Grouped-query heads: H_kv in [1, H] and dividing H (H == 0 launches nothing).
+inline bool heads_ok(int H, int H_kv) { return H == 0 || (H_kv >= 1 && H_kv <= H && H % H_kv == 0); }
+
 }  // namespace
 
 extern "C" {
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 200; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -67,11 +70,12 @@ const char* attn_status_string(int status) {
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-             int B, int H, int N, int Nk, int d, int dtype,
+             int B, int H, int H_kv, int N, int Nk, int d, int dtype,
              const int64_t* q_strides, const int64_t* k_strides,
              const int64_t* v_strides, const int64_t* o_strides,
              float scale, int causal, void* stream) {
   if (B < 0 || H < 0 || N < 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
   if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return fail(ATTN_ERR_UNSUPPORTED);
@@ -81,8 +85,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const int esize = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
   int64_t qs[3], ks[3], vs[3], os[3];
   strides_or_default(q_strides, H, N, d, qs);
-  strides_or_default(k_strides, H, Nk, d, ks);
-  strides_or_default(v_strides, H, Nk, d, vs);
+  strides_or_default(k_strides, H_kv, Nk, d, ks);
+  strides_or_default(v_strides, H_kv, Nk, d, vs);
   strides_or_default(o_strides, H, N, d, os);
   if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
     return fail(ATTN_ERR_UNSUPPORTED);
@@ -101,6 +105,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   p.o_sb = os[0]; p.o_sh = os[1]; p.o_sn = os[2];
   p.l_sb = (int64_t)H * N; p.l_sh = N; p.l_sn = 1;
   p.B = B; p.H = H; p.Nq = N; p.Nk = Nk;
+  p.kv_group = H / H_kv;
   p.scale_log2 = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_DTYPE_BF16) {
@@ -113,9 +118,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
-                    int max_seqlen_q, int max_seqlen_k, int H, int d, int dtype,
+                    int max_seqlen_q, int max_seqlen_k, int H, int H_kv, int d, int dtype,
                     float scale, int causal, void* stream) {
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || H < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
   if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
   if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED);
@@ -129,14 +135,15 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-  const int64_t tok = (int64_t)H * d;
+  const int64_t tok = (int64_t)H * d, ktok = (int64_t)H_kv * d;
   p.q_sn = tok; p.q_sh = d;
-  p.k_sn = tok; p.k_sh = d;
-  p.v_sn = tok; p.v_sh = d;
+  p.k_sn = ktok; p.k_sh = d;
+  p.v_sn = ktok; p.v_sh = d;
   p.o_sn = tok; p.o_sh = d;
   p.l_sn = H; p.l_sh = 1;
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
   p.B = num_seqs; p.H = H; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.kv_group = H / H_kv;
   p.n_rb = (max_seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM;
   p.scale_log2 = scale * kLog2e;
   return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, true, reinterpret_cast<hipStream_t>(stream)));
@@ -152,10 +159,11 @@ size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                       const int32_t* block_table, int max_pages_per_seq,
                       const int32_t* context_lens, int B, int num_pages, int page_size,
-                      int H, int d, int max_context_len, float scale,
+                      int H, int H_kv, int d, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0 || max_context_len < 0)
     return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
   if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
   if (page_size <= 0 || (page_size % 16) != 0) return fail(ATTN_ERR_UNSUPPORTED);
@@ -175,7 +183,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
   attn::DecodeParams p{};
   p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.o = o; p.lse = lse;
   p.block_table = block_table; p.context_lens = context_lens;
-  p.B = B; p.H = H; p.max_pages = max_pages_per_seq; p.page_size = page_size;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.max_pages = max_pages_per_seq; p.page_size = page_size;
   p.split_len = attn::kDecodeSplit;
   p.max_splits = max_context_len > 0 ? n_splits(max_context_len) : 0;
   const size_t slots = (size_t)B * H * p.max_splits;

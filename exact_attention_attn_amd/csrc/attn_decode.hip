@@ -13,7 +13,10 @@
 //    the next two chunks are already in flight while one is reduced;
 //  * q.k is a per-lane 8-term FMA plus a 4-step DPP reduction inside each 16-lane row;
 //  * every lane-row runs the online-softmax recurrence (section 2.2 of the same page)
-//    on its own tokens; the four rows are merged at the end with the same rescale.
+//    on its own tokens; the four rows are merged at the end with the same rescale;
+//  * grouped-query attention (section "GQA" of the same page): query head h reads KV
+//    head h / (H / H_kv) in place; the query heads sharing a KV head are adjacent
+//    wavefronts of one workgroup, so the repeated reads of a KV row hit in cache.
 // The second kernel merges the splits of each (sequence, head): with M = max_c m_c,
 // O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, lse = (M + log2 L) ln 2, in split
 // order (deterministic).  This is the online-softmax rescale applied to partial
@@ -62,17 +65,21 @@ struct Chunk {
   u32x4 v[NI];
 };
 
-template <int D>
+// One wavefront per (sequence, split, GW consecutive query heads).  The GW heads share
+// one KV head (GW divides H / H_kv), so each K/V row is loaded once for all of them.
+template <int D, int GW>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
   using C = Chunk<D>;
   constexpr int LPT = C::LPT, TPI = C::TPI, NI = C::NI;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int h = blockIdx.x * 4 + wave;  // head groups of one (sequence, split) are adjacent
-  const int split = blockIdx.y;          // in dispatch order, so a page is read by all of
-                                         // them at about the same time
+  const int hw = blockIdx.x * 4 + wave;  // head group of this wave; the groups of one
+  const int split = blockIdx.y;          // (sequence, split) are adjacent in dispatch
+                                         // order, so a page is read by all of them at
+                                         // about the same time
   const int b = blockIdx.z;
-  if (h >= p.H) return;  // no barriers in this kernel: waves are independent
+  const int h0 = hw * GW;                // first query head of this wave
+  if (h0 >= p.H) return;  // no barriers in this kernel: waves are independent
   const int ctx = p.context_lens[b];
   const int t_begin = split * p.split_len;
   if (t_begin >= ctx) return;
@@ -81,19 +88,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 
   const int g = lane / LPT;        // token row within an instruction
   const int cl = lane % LPT;       // 16-byte column chunk
-  const int64_t tok_stride = (int64_t)p.H * D;           // elements between slots
+  const int64_t tok_stride = (int64_t)p.H_kv * D;        // elements between slots
   const int64_t page_stride = (int64_t)p.page_size * tok_stride;
-  const int64_t lane_off = (int64_t)h * D + cl * 8;
+  const int hk = h0 / (p.H / p.H_kv);                     // the KV head of all GW heads
+  const int64_t lane_off = (int64_t)hk * D + cl * 8;
   const uint16_t* __restrict__ Kc = (const uint16_t*)p.k_cache;
   const uint16_t* __restrict__ Vc = (const uint16_t*)p.v_cache;
   const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_pages;
 
-  // q slice of this lane, pre-multiplied by nothing: scores are scaled after the sum
-  float qf[8];
-  {
-    const u32x4 u = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h) * D + cl * 8);
-    qf[0] = bf_lo(u.x); qf[1] = bf_hi(u.x); qf[2] = bf_lo(u.y); qf[3] = bf_hi(u.y);
-    qf[4] = bf_lo(u.z); qf[5] = bf_hi(u.z); qf[6] = bf_lo(u.w); qf[7] = bf_hi(u.w);
+  // q slices of this lane, one per head; scores are scaled after the sum
+  float qf[GW][8];
+#pragma unroll
+  for (int j = 0; j < GW; ++j) {
+    const u32x4 u = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h0 + j) * D + cl * 8);
+    qf[j][0] = bf_lo(u.x); qf[j][1] = bf_hi(u.x); qf[j][2] = bf_lo(u.y); qf[j][3] = bf_hi(u.y);
+    qf[j][4] = bf_lo(u.z); qf[j][5] = bf_hi(u.z); qf[j][6] = bf_lo(u.w); qf[j][7] = bf_hi(u.w);
   }
 
   auto load_chunk = [&](int u, C& c) {
@@ -115,53 +124,61 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     }
   };
 
-  float m2 = kNegInf, l = 0.f, acc[8];
+  float m2[GW], l[GW], acc[GW][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int j = 0; j < GW; ++j) {
+    m2[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
   const float c2 = p.scale_log2;
 
   auto consume = [&](int u, const C& c) {
     const int t0 = t_begin + 16 * u;
-    float s[NI];
-    float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const u32x4 w = c.k[i];
-      float d = qf[0] * bf_lo(w.x);
-      d = __builtin_fmaf(qf[1], bf_hi(w.x), d);
-      d = __builtin_fmaf(qf[2], bf_lo(w.y), d);
-      d = __builtin_fmaf(qf[3], bf_hi(w.y), d);
-      d = __builtin_fmaf(qf[4], bf_lo(w.z), d);
-      d = __builtin_fmaf(qf[5], bf_hi(w.z), d);
-      d = __builtin_fmaf(qf[6], bf_lo(w.w), d);
-      d = __builtin_fmaf(qf[7], bf_hi(w.w), d);
-      d = group_sum<LPT>(d);
-      const bool ok = t0 + i * TPI + g < t_end;
-      s[i] = ok ? d * c2 : kNegInf;
-      mx = fmaxf(mx, s[i]);
+    for (int j = 0; j < GW; ++j) {
+      float s[NI];
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const u32x4 w = c.k[i];
+        float d = qf[j][0] * bf_lo(w.x);
+        d = __builtin_fmaf(qf[j][1], bf_hi(w.x), d);
+        d = __builtin_fmaf(qf[j][2], bf_lo(w.y), d);
+        d = __builtin_fmaf(qf[j][3], bf_hi(w.y), d);
+        d = __builtin_fmaf(qf[j][4], bf_lo(w.z), d);
+        d = __builtin_fmaf(qf[j][5], bf_hi(w.z), d);
+        d = __builtin_fmaf(qf[j][6], bf_lo(w.w), d);
+        d = __builtin_fmaf(qf[j][7], bf_hi(w.w), d);
+        d = group_sum<LPT>(d);
+        const bool ok = t0 + i * TPI + g < t_end;
+        s[i] = ok ? d * c2 : kNegInf;
+        mx = fmaxf(mx, s[i]);
+      }
+      const float mnew = fmaxf(m2[j], mx);
+      const float muse = (mnew == kNegInf) ? 0.f : mnew;
+      const float alpha = exp2_fast(m2[j] - muse);
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float pv = exp2_fast(s[i] - muse);
+        rs += pv;
+        const u32x4 w = c.v[i];
+        acc[j][0] = __builtin_fmaf(pv, bf_lo(w.x), acc[j][0]);
+        acc[j][1] = __builtin_fmaf(pv, bf_hi(w.x), acc[j][1]);
+        acc[j][2] = __builtin_fmaf(pv, bf_lo(w.y), acc[j][2]);
+        acc[j][3] = __builtin_fmaf(pv, bf_hi(w.y), acc[j][3]);
+        acc[j][4] = __builtin_fmaf(pv, bf_lo(w.z), acc[j][4]);
+        acc[j][5] = __builtin_fmaf(pv, bf_hi(w.z), acc[j][5]);
+        acc[j][6] = __builtin_fmaf(pv, bf_lo(w.w), acc[j][6]);
+        acc[j][7] = __builtin_fmaf(pv, bf_hi(w.w), acc[j][7]);
+      }
+      l[j] = l[j] * alpha + rs;
+      m2[j] = mnew;
     }
-    const float mnew = fmaxf(m2, mx);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = exp2_fast(m2 - muse);
-    float rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float pv = exp2_fast(s[i] - muse);
-      rs += pv;
-      const u32x4 w = c.v[i];
-      acc[0] = __builtin_fmaf(pv, bf_lo(w.x), acc[0]);
-      acc[1] = __builtin_fmaf(pv, bf_hi(w.x), acc[1]);
-      acc[2] = __builtin_fmaf(pv, bf_lo(w.y), acc[2]);
-      acc[3] = __builtin_fmaf(pv, bf_hi(w.y), acc[3]);
-      acc[4] = __builtin_fmaf(pv, bf_lo(w.z), acc[4]);
-      acc[5] = __builtin_fmaf(pv, bf_hi(w.z), acc[5]);
-      acc[6] = __builtin_fmaf(pv, bf_lo(w.w), acc[6]);
-      acc[7] = __builtin_fmaf(pv, bf_hi(w.w), acc[7]);
-    }
-    l = l * alpha + rs;
-    m2 = mnew;
   };
 
   // three chunks in flight: consume u while u+1 and u+2 load
@@ -180,30 +197,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   if (u < nchunks) consume(u, c0);
   if (u + 1 < nchunks) consume(u + 1, c1);
 
-  // merge the lane rows (token rows g) of this wavefront
+  // merge the lane rows (token rows g) of this wavefront, head by head
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(m2, off);
-    const float lo = __shfl_xor(l, off);
-    const float mm = fmaxf(m2, mo);
-    const float mu = (mm == kNegInf) ? 0.f : mm;
-    const float a0 = exp2_fast(m2 - mu), a1 = exp2_fast(mo - mu);
+  for (int j = 0; j < GW; ++j) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ao = __shfl_xor(acc[e], off);
-      acc[e] = acc[e] * a0 + ao * a1;
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(m2[j], off);
+      const float lo = __shfl_xor(l[j], off);
+      const float mm = fmaxf(m2[j], mo);
+      const float mu = (mm == kNegInf) ? 0.f : mm;
+      const float a0 = exp2_fast(m2[j] - mu), a1 = exp2_fast(mo - mu);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(acc[j][e], off);
+        acc[j][e] = acc[j][e] * a0 + ao * a1;
+      }
+      l[j] = l[j] * a0 + lo * a1;
+      m2[j] = mm;
     }
-    l = l * a0 + lo * a1;
-    m2 = mm;
+    const int64_t slot = ((int64_t)b * p.H + h0 + j) * p.max_splits + split;
+    if (g == 0) {
+      float* dst = p.ws_acc + slot * D + cl * 8;
+      *(float4*)dst = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *(float4*)(dst + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+    }
+    if (lane == 0) *(float2*)(p.ws_ml + slot * 2) = make_float2(m2[j], l[j]);
   }
-
-  const int64_t slot = ((int64_t)b * p.H + h) * p.max_splits + split;
-  if (g == 0) {
-    float* dst = p.ws_acc + slot * D + cl * 8;
-    *(float4*)dst = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *(float4*)(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  }
-  if (lane == 0) *(float2*)(p.ws_ml + slot * 2) = make_float2(m2, l);
 }
 
 // One wavefront per (sequence, head); lane owns D/64 columns.
@@ -239,13 +258,28 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams 
   if (p.lse != nullptr && lane == 0) p.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
+template <int D, int GW>
+hipError_t launch_split(const DecodeParams& p, hipStream_t s) {
+  const int waves = p.H / GW;  // head groups per (sequence, split)
+  dim3 grid((unsigned)((waves + 3) / 4), (unsigned)p.max_splits, (unsigned)p.B);
+  hipLaunchKernelGGL((decode_split_kernel<D, GW>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   if (p.B <= 0 || p.H <= 0) return hipSuccess;
   if (p.max_splits > 0) {
-    dim3 grid((unsigned)((p.H + 3) / 4), (unsigned)p.max_splits, (unsigned)p.B);
-    hipLaunchKernelGGL((decode_split_kernel<D>), grid, dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
+    // query heads per wavefront: the largest of 4 (d = 64 only: register budget), 2, 1
+    // that divides the group size
+    const int group = p.H / p.H_kv;
+    hipError_t e;
+    if (D == 64 && group % 4 == 0)
+      e = launch_split<D, 4>(p, s);
+    else if (group % 2 == 0)
+      e = launch_split<D, 2>(p, s);
+    else
+      e = launch_split<D, 1>(p, s);
     if (e != hipSuccess) return e;
   }
   const int nbh = p.B * p.H;

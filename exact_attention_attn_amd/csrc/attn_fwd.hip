@@ -53,25 +53,35 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast
 
 // Block index -> (row block, batch/sequence, head).  Workgroups are dispatched
 // round-robin over the 8 XCDs (bid % 8), each with its own L2.  When the number of
-// (batch, head) pairs is a multiple of 8, XCD x takes pairs x, x+8, x+16, ... one after
-// the other, with all row blocks of a pair back to back, so the K/V of the pairs in
-// flight stay in that XCD's L2.  Causal launches take the heaviest (last) row block of
-// a pair first.
+// (batch, KV head) pairs is a multiple of 8, XCD x takes KV pairs x, x+8, x+16, ... one
+// after the other; for each, the query heads reading that KV head (one under multi-head
+// attention, H / H_kv under grouped-query attention) run back to back, each with all
+// its row blocks, so the K/V in flight stay in that XCD's L2 and every XCD gets an even
+// share of heads and sequences.  Causal launches take the heaviest (last) row block of
+// a head first.
 template <bool CAUSAL>
 __device__ __forceinline__ void block_coords(const FwdParams& p, int& rb, int& b, int& h) {
-  const int npairs = p.H * p.B;
+  const int G = p.kv_group;
+  const int hkv = p.H / G;
+  const int nkv = hkv * p.B;
   const int bid = blockIdx.x;
-  int pair, rbi;
-  if ((npairs & 7) == 0) {
+  int rbi;
+  if ((nkv & 7) == 0) {
     const int x = bid & 7, i = bid >> 3;
-    pair = x + 8 * (i / p.n_rb);
-    rbi = i - (i / p.n_rb) * p.n_rb;
+    const int per = G * p.n_rb;        // blocks per KV pair
+    const int kvp = x + 8 * (i / per);
+    const int r = i - (i / per) * per;
+    const int member = r / p.n_rb;
+    rbi = r - member * p.n_rb;
+    b = kvp / hkv;
+    h = (kvp - b * hkv) * G + member;
   } else {
-    pair = bid % npairs;
+    const int npairs = p.H * p.B;
+    const int pair = bid % npairs;
     rbi = bid / npairs;
+    b = pair / p.H;
+    h = pair - b * p.H;
   }
-  b = pair / p.H;
-  h = pair - b * p.H;
   rb = CAUSAL ? (p.n_rb - 1 - rbi) : rbi;
 }
 
@@ -79,22 +89,23 @@ template <bool VARLEN>
 __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int h, int& Lq, int& Lk,
                                            int64_t& qoff, int64_t& koff, int64_t& voff,
                                            int64_t& ooff, int64_t& loff) {
+  const int hk = h / p.kv_group;  // KV head of query head h (grouped-query attention)
   if (VARLEN) {
     const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
     const int k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
     Lq = q1 - q0;
     Lk = k1 - k0;
     qoff = (int64_t)q0 * p.q_sn + (int64_t)h * p.q_sh;
-    koff = (int64_t)k0 * p.k_sn + (int64_t)h * p.k_sh;
-    voff = (int64_t)k0 * p.v_sn + (int64_t)h * p.v_sh;
+    koff = (int64_t)k0 * p.k_sn + (int64_t)hk * p.k_sh;
+    voff = (int64_t)k0 * p.v_sn + (int64_t)hk * p.v_sh;
     ooff = (int64_t)q0 * p.o_sn + (int64_t)h * p.o_sh;
     loff = (int64_t)q0 * p.l_sn + (int64_t)h * p.l_sh;
   } else {
     Lq = p.Nq;
     Lk = p.Nk;
     qoff = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    koff = (int64_t)b * p.k_sb + (int64_t)h * p.k_sh;
-    voff = (int64_t)b * p.v_sb + (int64_t)h * p.v_sh;
+    koff = (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+    voff = (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
     ooff = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
     loff = (int64_t)b * p.l_sb + (int64_t)h * p.l_sh;
   }

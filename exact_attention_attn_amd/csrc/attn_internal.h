@@ -10,7 +10,8 @@ namespace attn {
 // Parameters of one dense or varlen forward launch.  Strides are in elements.
 // Dense: tensor (b, h, n, :) starts at b*sb + h*sh + n*sn.
 // Varlen: token t of head h starts at t*sn + h*sh (sb unused); sequence s owns
-// tokens [cu[s], cu[s+1]).
+// tokens [cu[s], cu[s+1]).  For K and V, h is the KV head: query head h reads KV head
+// h / kv_group.
 struct FwdParams {
   const void* q;
   const void* k;
@@ -29,12 +30,13 @@ struct FwdParams {
   int Nq;     // dense: query length; varlen: max_seqlen_q
   int Nk;     // dense: key length;   varlen: max_seqlen_k
   int n_rb;   // query row blocks per (b, h)
+  int kv_group;  // query heads per KV head (1: multi-head attention)
   float scale_log2;  // scale * log2(e): scores are handled in base-2 units
 };
 
 struct DecodeParams {
   const void* q;        // [B, H, d]
-  const void* k_cache;  // [P, page, H, d]
+  const void* k_cache;  // [P, page, H_kv, d]
   const void* v_cache;
   void* o;              // [B, H, d]
   float* lse;           // [B, H] or null
@@ -43,6 +45,7 @@ struct DecodeParams {
   float* ws_acc;        // [B, H, max_splits, d]   unnormalised partial outputs
   float* ws_ml;         // [B, H, max_splits, 2]   partial (m, l), base-2 units
   int B, H;
+  int H_kv;             // query head h reads KV head h / (H / H_kv)
   int max_pages;
   int page_size;
   int split_len;        // tokens per split, a multiple of 16

@@ -36,6 +36,12 @@
  * - Supported head dimension d: 64 or 128.  Other values are rejected
  *   (ATTN_ERR_UNSUPPORTED), never computed on a truncated tile.
  * - scale must be finite and > 0 (the pages use 1/sqrt(d)).
+ * - Grouped-query attention (dlog.com.cn page, section "GQA: handled natively by the
+ *   kernel, K/V not expanded"): K and V carry H_kv heads, H_kv divides H, and query
+ *   head h reads KV head h / (H / H_kv) -- the head order of expanding each KV head
+ *   H / H_kv times.  H_kv == H is plain multi-head attention, H_kv == 1 multi-query.
+ *   K/V are never expanded in memory.  H_kv < 1 or H not a multiple of H_kv returns
+ *   ATTN_ERR_INVALID_ARG (when H > 0).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -59,10 +65,11 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
 /*
  * attn_fwd — dense batched attention.
  *
- * q, o : logical [B, H, N, d];  k, v : logical [B, H, Nk, d]; element type `dtype`
+ * q, o : logical [B, H, N, d];  k, v : logical [B, H_kv, Nk, d]; element type `dtype`
  *        (o has q's type).  The d dimension must be contiguous.
  * *_strides : three int64 element strides for the (b, h, n) dimensions of that tensor,
- *        or NULL for a contiguous [B, H, N(k), d] tensor.  Strides make the
+ *        or NULL for a contiguous [B, H, N, d] (q, o) / [B, H_kv, Nk, d] (k, v)
+ *        tensor.  Strides make the
  *        [B, N, H, d] layout of the flash-attn interface and packed QKV / KV
  *        tensors ([B, N, 3, H, d], [B, N, 2, H, d]; page section 3.2) usable
  *        without copies.  Every row start must be 16-byte aligned.
@@ -71,7 +78,7 @@ typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
  * B, H, N, Nk may be 0 (nothing is launched).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-             int B, int H, int N, int Nk, int d, int dtype,
+             int B, int H, int H_kv, int N, int Nk, int d, int dtype,
              const int64_t* q_strides, const int64_t* k_strides,
              const int64_t* v_strides, const int64_t* o_strides,
              float scale, int causal, void* stream);
@@ -79,7 +86,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * attn_fwd_varlen — packed variable-length batch (bfloat16).
  *
- * q, o : [total_q, H, d] contiguous;  k, v : [total_k, H, d] contiguous.
+ * q, o : [total_q, H, d] contiguous;  k, v : [total_k, H_kv, d] contiguous.
  * cu_seqlens_q, cu_seqlens_k : int32 [num_seqs + 1] device arrays of prefix sums;
  *        sequence s owns Q rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and K/V rows
  *        [cu_seqlens_k[s], cu_seqlens_k[s+1]) (the page's example [0, 3, 7] is two
@@ -90,7 +97,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
-                    int max_seqlen_q, int max_seqlen_k, int H, int d, int dtype,
+                    int max_seqlen_q, int max_seqlen_k, int H, int H_kv, int d, int dtype,
                     float scale, int causal, void* stream);
 
 /*
@@ -103,7 +110,7 @@ size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len
  * attn_decode_paged — decode step over a paged KV cache (bfloat16).
  *
  * q, o : [B, H, d] contiguous (one new query token per sequence).
- * k_cache, v_cache : [num_pages, page_size, H, d] contiguous page pools.
+ * k_cache, v_cache : [num_pages, page_size, H_kv, d] contiguous page pools.
  * block_table : int32 [B, max_pages_per_seq]; token t of sequence b lives in page
  *        block_table[b][t / page_size], slot t % page_size.  Entries past
  *        ceil(context_lens[b] / page_size) are never read.
@@ -119,7 +126,7 @@ size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                       const int32_t* block_table, int max_pages_per_seq,
                       const int32_t* context_lens, int B, int num_pages, int page_size,
-                      int H, int d, int max_context_len, float scale,
+                      int H, int H_kv, int d, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */

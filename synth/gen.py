@@ -102,12 +102,15 @@ class Dense:
 
 
 def dense(B: int, H: int, N: int, d: int, dtype: str = "bf16", causal: bool = False,
-          scale: float | None = None, seed: int = 0, Nk: int | None = None) -> Dense:
+          scale: float | None = None, seed: int = 0, Nk: int | None = None,
+          H_kv: int | None = None) -> Dense:
+    """Q [B, H, N, d]; K, V [B, H_kv, Nk, d] (H_kv defaults to H)."""
     Nk = N if Nk is None else Nk
+    H_kv = H if H_kv is None else H_kv
     bf = dtype == "bf16"
     q = normal(seed, T_Q, (B, H, N, d), bf)
-    k = normal(seed, T_K, (B, H, Nk, d), bf)
-    v = normal(seed, T_V, (B, H, Nk, d), bf)
+    k = normal(seed, T_K, (B, H_kv, Nk, d), bf)
+    v = normal(seed, T_V, (B, H_kv, Nk, d), bf)
     return Dense(B, H, N, d, dtype, causal, 1.0 / math.sqrt(d) if scale is None else scale, q, k, v, Nk)
 
 
@@ -149,10 +152,12 @@ def cu_from_lens(lens) -> np.ndarray:
 
 def varlen(num_seqs: int = 16, lmin: int = 128, lmax: int = 4096, H: int = 32, d: int = 128,
            causal: bool = True, scale: float | None = None, seed: int = 0,
-           lens=None, lens_k=None) -> Varlen:
+           lens=None, lens_k=None, H_kv: int | None = None) -> Varlen:
     """Draw order: lengths = rng.integers(lmin, lmax, num_seqs, endpoint=True); then Q, K, V.
 
-    ``lens`` / ``lens_k`` override the drawn lengths (edge-case tests)."""
+    ``lens`` / ``lens_k`` override the drawn lengths (edge-case tests).  K and V carry
+    H_kv heads (default H)."""
+    H_kv = H if H_kv is None else H_kv
     rng = np.random.default_rng(seed)
     if lens is None:
         lens = rng.integers(lmin, lmax, size=num_seqs, endpoint=True)
@@ -161,8 +166,8 @@ def varlen(num_seqs: int = 16, lmin: int = 128, lmax: int = 4096, H: int = 32, d
     cu_q, cu_k = cu_from_lens(lens), cu_from_lens(lens_k)
     tq, tk = int(cu_q[-1]), int(cu_k[-1])
     q = normal(seed, T_Q, (tq, H, d), True)
-    k = normal(seed, T_K, (tk, H, d), True)
-    v = normal(seed, T_V, (tk, H, d), True)
+    k = normal(seed, T_K, (tk, H_kv, d), True)
+    v = normal(seed, T_V, (tk, H_kv, d), True)
     return Varlen(H, d, causal, 1.0 / math.sqrt(d) if scale is None else scale,
                   lens, lens_k, cu_q, cu_k, q, k, v)
 
@@ -198,10 +203,12 @@ class Paged:
 
 def paged(B: int = 64, H: int = 32, d: int = 128, ctx_min: int = 512, ctx_max: int = 8192,
           page: int = 16, scale: float | None = None, seed: int = 0, poison: bool = True,
-          ctx=None, identity: bool = False, with_pool: bool = True) -> Paged:
+          ctx=None, identity: bool = False, with_pool: bool = True, H_kv: int | None = None) -> Paged:
     """Draw order: ctx = rng.integers(ctx_min, ctx_max, B, endpoint=True); then the page
     permutation rng.permutation(num_pages), dealt out to sequences in order; then q,
-    k_cache, v_cache.  ``identity`` uses pages 0..n-1 in order instead of the permutation."""
+    k_cache, v_cache.  ``identity`` uses pages 0..n-1 in order instead of the permutation.
+    The pools carry H_kv heads (default H)."""
+    H_kv = H if H_kv is None else H_kv
     rng = np.random.default_rng(seed)
     if ctx is None:
         ctx = rng.integers(ctx_min, ctx_max, size=B, endpoint=True)
@@ -220,8 +227,8 @@ def paged(B: int = 64, H: int = 32, d: int = 128, ctx_min: int = 512, ctx_max: i
     q = normal(seed, T_Q, (B, H, d), True)
     kc = vc = None
     if with_pool:
-        kc = normal(seed, T_KCACHE, (num_pages + 1, page, H, d), True)
-        vc = normal(seed, T_VCACHE, (num_pages + 1, page, H, d), True)
+        kc = normal(seed, T_KCACHE, (num_pages + 1, page, H_kv, d), True)
+        vc = normal(seed, T_VCACHE, (num_pages + 1, page, H_kv, d), True)
         if poison:
             kc[num_pages] = BF16_NAN
             vc[num_pages] = BF16_NAN
@@ -248,6 +255,8 @@ WORKLOADS = {
     "c3": "long causal bf16 B=1 H=32 N=8192 d=128",
     "c4": "varlen causal bf16 16 seqs len U[128,4096] H=32 d=128",
     "c5": "paged decode bf16 64 seqs ctx U[512,8192] H=32 d=128 page 16",
+    "gqa_decode": "paged decode bf16 64 seqs ctx U[512,8192] H=16 H_kv=8 d=128 page 16 "
+                  "(the page's 16-query-head / 8-KV-head model shape)",
 }
 
 
@@ -262,4 +271,6 @@ def workload(name: str, seed: int = 0, **kw):
         return varlen(16, 128, 4096, 32, 128, True, seed=seed)
     if name == "c5":
         return paged(64, 32, 128, 512, 8192, 16, seed=seed, **kw)
+    if name == "gqa_decode":
+        return paged(64, 16, 128, 512, 8192, 16, seed=seed, H_kv=8, **kw)
     raise KeyError(name)

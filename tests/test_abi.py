@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for n in header_functions():
         assert hasattr(lib, n), n
     assert set(header_functions()) == set(attn.EXPORTS)
-    assert lib.attn_version() >= 100
+    assert lib.attn_version() >= 200   # 2.0: grouped-query heads in all three entries
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
@@ -36,10 +36,10 @@ FAKE_ODD = ctypes.c_void_p((1 << 20) + 2)
 
 
 def fwd(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=1, N=64, Nk=64, d=128,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=4, Hkv=4, N=64, Nk=64, d=128,
              dtype=attn.ATTN_DTYPE_BF16, qs=None, ks=None, vs=None, os_=None, scale=0.1, causal=0)
     a.update(kw)
-    return attn.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["Nk"],
+    return attn.load().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["Nk"],
                                 a["d"], a["dtype"], a["qs"], a["ks"], a["vs"], a["os_"], a["scale"],
                                 a["causal"], None)
 
@@ -64,19 +64,26 @@ def fwd(**kw):
     (dict(qs=(ctypes.c_int64 * 3)(64 * 128, 128 * 64, 129)), attn.ATTN_ERR_UNSUPPORTED),
     (dict(ks=(ctypes.c_int64 * 3)(-128, 128, 128)), attn.ATTN_ERR_UNSUPPORTED),
     (dict(lse=ctypes.c_void_p((1 << 20) + 1)), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), attn.ATTN_ERR_INVALID_ARG),      # grouped-query heads must divide H
+    (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=8), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=-4), attn.ATTN_ERR_INVALID_ARG),
     (dict(B=0), attn.ATTN_OK),          # nothing to do: no launch
     (dict(N=0), attn.ATTN_OK),
+    (dict(N=0, Hkv=2), attn.ATTN_OK),
+    (dict(N=0, Hkv=1), attn.ATTN_OK),
 ])
 def test_fwd_rejects_before_launch(kw, status):
     assert fwd(**kw) == status
 
 
 def varlen(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cq=FAKE, ck=FAKE, S=2, mq=16, mk=16, H=2, d=128,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cq=FAKE, ck=FAKE, S=2, mq=16, mk=16, H=2, Hkv=2, d=128,
              dtype=attn.ATTN_DTYPE_BF16, scale=0.1, causal=1)
     a.update(kw)
     return attn.load().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["S"],
-                                       a["mq"], a["mk"], a["H"], a["d"], a["dtype"], a["scale"], a["causal"], None)
+                                       a["mq"], a["mk"], a["H"], a["Hkv"], a["d"], a["dtype"], a["scale"],
+                                       a["causal"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -88,6 +95,8 @@ def varlen(**kw):
     (dict(mq=-1), attn.ATTN_ERR_INVALID_ARG),
     (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
     (dict(q=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(Hkv=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
     (dict(S=0), attn.ATTN_OK),
     (dict(mq=0), attn.ATTN_OK),
 ])
@@ -97,11 +106,11 @@ def test_varlen_rejects_before_launch(kw, status):
 
 def decode(**kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, bt=FAKE, maxp=8, cl=FAKE, B=2, P=16, page=16, H=2,
-             d=128, maxctx=128, scale=0.1, ws=FAKE, wsb=1 << 30)
+             Hkv=2, d=128, maxctx=128, scale=0.1, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return attn.load().attn_decode_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["bt"], a["maxp"], a["cl"],
-                                         a["B"], a["P"], a["page"], a["H"], a["d"], a["maxctx"], a["scale"],
-                                         a["ws"], a["wsb"], None)
+                                         a["B"], a["P"], a["page"], a["H"], a["Hkv"], a["d"], a["maxctx"],
+                                         a["scale"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -117,6 +126,8 @@ def decode(**kw):
     (dict(B=-2), attn.ATTN_ERR_INVALID_ARG),
     (dict(scale=-0.5), attn.ATTN_ERR_INVALID_ARG),
     (dict(kc=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(Hkv=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=4), attn.ATTN_ERR_INVALID_ARG),
     (dict(B=0), attn.ATTN_OK),
 ])
 def test_decode_rejects_before_launch(kw, status):

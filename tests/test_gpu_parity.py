@@ -303,3 +303,71 @@ def test_decode_deterministic(A):
     o2, l2 = A.attn_decode_paged(*args, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ grouped-query attention
+
+@pytest.mark.parametrize("H,Hkv,N,Nk,causal,d", [
+    (16, 8, 1000, 1000, True, 128),    # the page's 16 query heads sharing 8 KV heads
+    (16, 8, 777, 1333, False, 128),
+    (32, 4, 513, 513, True, 128),
+    (8, 1, 300, 300, True, 64),        # multi-query
+    (6, 3, 200, 257, True, 64),        # 12 (b, h) pairs: not a multiple of 8
+])
+def test_dense_gqa_bf16(A, H, Hkv, N, Nk, causal, d):
+    w = synth.dense(2, H, N, d, "bf16", causal, seed=40, Nk=Nk, H_kv=Hkv)
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+@pytest.mark.parametrize("H,Hkv,causal", [(4, 2, True), (4, 1, False)])
+def test_dense_gqa_fp32(A, H, Hkv, causal):
+    w = synth.dense(2, H, 100, 64, "f32", causal, seed=41, Nk=130, H_kv=Hkv)
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal)
+    assert_close("O", o, ro, TOL_F32)
+    assert_close("lse", lse, rl, TOL_F32)
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(8, 2, 128), (16, 8, 64), (4, 1, 128)])
+def test_varlen_gqa(A, H, Hkv, d):
+    import torch
+    w = synth.varlen(H=H, d=d, causal=True, seed=42, lens=[5, 130, 64, 1, 700, 257], H_kv=Hkv)
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, True)
+    assert_close("O", host(o), ro, TOL_BF16_O)
+    assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(16, 8, 128), (8, 1, 64), (32, 4, 128)])
+def test_decode_gqa(A, H, Hkv, d):
+    import torch
+    w = synth.paged(H=H, d=d, seed=43, ctx=[1, 17, 600, 1024, 33, 512, 513, 2000], H_kv=Hkv)
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), int(w.context_lens.max()), scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+def test_gqa_decode_full_sampled(A):
+    """The grouped-query decode workload the bench times (64 sequences, 16 query heads
+    on 8 KV heads), every sequence, sampled heads."""
+    import torch
+    w = synth.workload("gqa_decode")
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), int(w.context_lens.max()), scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale,
+                                           heads=[0, 1, 7, 14, 15])
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
