@@ -9,6 +9,8 @@ Contents
 ``attention``      the plain definition softmax(scale * Q K^T) V, two-pass, fp64
 ``online``         the tiled online-softmax recurrence, used only to pin ``attention``
 
+``attention.store_kvcache`` is the plain scatter of new K/V rows into the page pools.
+
 Every function cites the passage of the source pages it follows.
 """
 from .attention import (  # noqa: F401
@@ -21,5 +23,6 @@ from .attention import (  # noqa: F401
     gather_paged,
     kv_head,
     probabilities,
+    store_kvcache,
 )
 from .online import online_attention  # noqa: F401

@@ -198,3 +198,21 @@ def attention_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale
             ob, lb = attention_rows(q[b, h][None, :], kb, vb, scale, False)
             o[b, h], lse[b, h] = ob[0], lb[0]
     return o, lse
+
+
+def store_kvcache(k, v, k_cache, v_cache, slot_mapping):
+    """Write one step's new K/V rows into the paged pools ("From standard Attention to
+    FlashAttention and paged execution", the attention step of the v3 engine: the
+    step's k/v are first written into the paged KV cache through slot_mapping, every
+    step, prefill and decode alike).  k, v [T, H_kv, d]; pools [pages, page, H_kv, d].
+    Reading where the page is silent: slot_mapping[t] is the flat slot
+    page * page_size + offset of token t's row; a slot outside [0, pages * page) (for
+    instance -1, padding) is skipped.  Returns new pool arrays; the inputs are not
+    modified."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    pages, page = kc.shape[0], kc.shape[1]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if 0 <= slot < pages * page:
+            kc[slot // page, slot % page] = k[t]
+            vc[slot // page, slot % page] = v[t]
+    return kc, vc

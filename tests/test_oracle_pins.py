@@ -432,3 +432,39 @@ def test_gqa_paged_decode_brute_force():
             vs = [vc[bt[b, t // page], t % page, hk].tolist() for t in range(c)]
             ob, lb = _brute([q[b, h].tolist()], ks, vs, 0.6, False)
             assert np.abs(o[b, h] - ob[0]).max() < TIGHT and abs(l[b, h] - lb[0]) < TIGHT
+
+
+# ----------------------------------------------------------------- store_kvcache
+
+def test_store_kvcache_then_gather_round_trip():
+    """Rows scattered through slot_mapping come back, in token order, from the block-
+    table gather of the paged layout (token t of a sequence in page block_table[t //
+    page], slot t % page)."""
+    r = rng(40)
+    page, Hkv, d = 4, 2, 3
+    P = 6
+    bt = np.array([4, 1, 5], dtype=np.int32)         # one sequence, 10 tokens, 3 pages
+    T = 10
+    slots = np.array([bt[t // page] * page + t % page for t in range(T)], dtype=np.int64)
+    k, v = r.normal(size=(T, Hkv, d)), r.normal(size=(T, Hkv, d))
+    kc0, vc0 = r.normal(size=(P, page, Hkv, d)), r.normal(size=(P, page, Hkv, d))
+    kc, vc = oracle.store_kvcache(k, v, kc0, vc0, slots)
+    for h in range(Hkv):
+        assert np.array_equal(oracle.gather_paged(kc[:, :, h], bt, T, page), k[:, h])
+        assert np.array_equal(oracle.gather_paged(vc[:, :, h], bt, T, page), v[:, h])
+    # every other slot is untouched, and the inputs are not modified
+    written = np.zeros((P, page), dtype=bool)
+    written[slots // page, slots % page] = True
+    assert np.array_equal(kc[~written], kc0[~written]) and np.array_equal(vc[~written], vc0[~written])
+
+
+def test_store_kvcache_skips_padding_and_out_of_range_slots():
+    r = rng(41)
+    k, v = r.normal(size=(4, 1, 2)), r.normal(size=(4, 1, 2))
+    kc0, vc0 = r.normal(size=(2, 4, 1, 2)), r.normal(size=(2, 4, 1, 2))
+    kc, vc = oracle.store_kvcache(k, v, kc0, vc0, np.array([-1, 8, 3, -7]))
+    expect_k = kc0.copy()
+    expect_k[0, 3] = k[2]                             # only slot 3 is in range
+    assert np.array_equal(kc, expect_k)
+    assert np.array_equal(vc[0, 3], v[2]) and np.array_equal(np.delete(vc.reshape(8, 1, 2), 3, 0),
+                                                              np.delete(vc0.reshape(8, 1, 2), 3, 0))
