@@ -7,6 +7,7 @@ One step = one call of each entry point on its workload, inputs resident in HBM:
   attn_decode_paged  64 sequences, context U[512,8192], 16-token pages, H=32 d=128 bf16
                      (headline, HBM GB/s)
   attn_decode_paged  the same lengths with 16 query heads on 8 KV heads (grouped-query)
+  attn_store_kvcache the varlen batch's 34069 new K/V rows written into 16-token pages
 
 W untimed warm-up steps, then K timed steps; every kernel call is bracketed by HIP
 events on the stream it runs on.  Prints ONE JSON line.  `value` is the dense
@@ -109,7 +110,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa"], default=None,
+    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache"], default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
@@ -163,6 +164,11 @@ def main() -> int:
     w6.k_cache = w6.v_cache = None
     log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
 
+    w7 = synth.workload("store_prefill")
+    k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
+    sl7 = torch.from_numpy(w7.slot_mapping).cuda()
+    log(f"[bench] store_kvcache workload ready ({time.perf_counter() - t:.1f} s)")
+
     def run_fwd():
         attn.attn_fwd(q3, k3, v3, scale=w3.scale, causal=True, out=o3, lse=l3)
 
@@ -175,7 +181,11 @@ def main() -> int:
     def run_decode_gqa():
         attn.attn_decode_paged(q6, kc6, vc6, bt6, cl6, maxctx6, scale=w6.scale, workspace=ws6, out=o6, lse=l6)
 
-    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa)]
+    def run_store():
+        attn.attn_store_kvcache(k7, v7, kc7, vc7, sl7)
+
+    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa),
+             ("store_kvcache", run_store)]
     if args.only:
         parts = [p for p in parts if p[0] == args.only]
 
@@ -241,6 +251,12 @@ def main() -> int:
                              "ms": ms["decode_gqa"].mean(), "GB/s": by6 / t6 / 1e9, "peak": PEAK_HBM_GBS,
                              "frac": by6 / t6 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by6,
                              "note": "KV bytes counted once per KV head (grouped-query)"}
+    if "store_kvcache" in ms:
+        t7 = ms["store_kvcache"].mean() / 1e3
+        by7 = 4 * w7.T * w7.H_kv * w7.d * 2 + 8 * w7.T   # K and V read and written once, slots read
+        res["store_kvcache"] = {"workload": f"{w7.T} tokens H_kv=32 d=128 bf16 into 16-token pages",
+                                "ms": ms["store_kvcache"].mean(), "GB/s": by7 / t7 / 1e9, "peak": PEAK_HBM_GBS,
+                                "frac": by7 / t7 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by7}
     res["wall_s_timed"] = wall
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")

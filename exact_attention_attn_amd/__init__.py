@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     attn_decode_paged_workspace_size,
     attn_fwd,
     attn_fwd_varlen,
+    attn_store_kvcache,
     load,
     status_string,
 )

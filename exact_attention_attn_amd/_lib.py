@@ -18,7 +18,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
-           "attn_status_string", "attn_version")
+           "attn_store_kvcache", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -46,6 +46,9 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    i64 = ctypes.c_int64
+    lib.attn_store_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
+    lib.attn_store_kvcache.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -185,3 +188,32 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "attn_decode_paged")
     return o, (lse if with_lse else None)
+
+
+def attn_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    """Write new K/V rows into the page pools.  k, v [T, H_kv, d] (token stride free,
+    [H_kv, d] contiguous; e.g. slices of a fused QKV output); k_cache/v_cache
+    [num_pages, page, H_kv, d] contiguous, written in place; slot_mapping int64 [T]
+    (slot = page * page_size + offset; out-of-pool slots such as -1 are skipped)."""
+    torch = _torch()
+    lib = load()
+    T, Hkv, d = k.shape
+    if v.shape != k.shape:
+        raise ValueError("k and v must have the same shape [T, H_kv, d]")
+    num_pages, page = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.shape[2:] != (Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("pools must be [num_pages, page, H_kv, d] matching k")
+    for t in (k, v):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("each token's [H_kv, d] row must be contiguous")
+    for t in (k_cache, v_cache, slot_mapping):
+        if not t.is_contiguous():
+            raise ValueError("pools and slot_mapping must be contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise TypeError("slot_mapping must be int64 [T]")
+    if k.dtype != k_cache.dtype or v.dtype != k.dtype or v_cache.dtype != k.dtype:
+        raise TypeError("k, v and the pools must share a dtype")
+    rc = lib.attn_store_kvcache(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, d,
+                                k.stride(0), v.stride(0), num_pages, page, _dtype_code(k), _stream(stream))
+    _check(rc, "attn_store_kvcache")
+    return k_cache, v_cache

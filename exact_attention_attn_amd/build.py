@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_kvcache.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code (-packed-fp32-ops).

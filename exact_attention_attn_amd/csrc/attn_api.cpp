@@ -193,4 +193,31 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
   return check_launch(attn::launch_decode_paged(p, d, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int T, int H_kv, int d,
+                       int64_t k_token_stride, int64_t v_token_stride,
+                       int num_pages, int page_size, int dtype, void* stream) {
+  if (T < 0 || H_kv < 0 || d < 0 || num_pages < 0 || page_size < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F32) return fail(ATTN_ERR_UNSUPPORTED);
+  const int esize = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  const int64_t row = (int64_t)H_kv * d * esize;
+  if (T == 0 || row == 0 || (int64_t)num_pages * page_size == 0) return ATTN_OK;  // nothing to write
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(ATTN_ERR_INVALID_ARG);
+  if (k_token_stride < (int64_t)H_kv * d || v_token_stride < (int64_t)H_kv * d) return fail(ATTN_ERR_INVALID_ARG);
+  if ((row & 15) != 0 || row > INT32_MAX || ((k_token_stride * esize) & 15) != 0 || ((v_token_stride * esize) & 15) != 0)
+    return fail(ATTN_ERR_UNSUPPORTED);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return fail(ATTN_ERR_UNSUPPORTED);
+  if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(ATTN_ERR_INVALID_ARG);
+
+  attn::StoreParams p{};
+  p.k = k; p.v = v; p.k_cache = k_cache; p.v_cache = v_cache;
+  p.slot_mapping = slot_mapping;
+  p.k_stride_bytes = k_token_stride * esize;
+  p.v_stride_bytes = v_token_stride * esize;
+  p.num_slots = (int64_t)num_pages * page_size;
+  p.T = T;
+  p.row_bytes = (int)row;
+  return check_launch(attn::launch_store_kvcache(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -53,10 +53,24 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Parameters of one store_kvcache launch.  Byte strides; rows are 16-byte multiples.
+struct StoreParams {
+  const void* k;            // token t's K row at k + t * k_stride_bytes
+  const void* v;
+  void* k_cache;            // slot s's row at k_cache + s * row_bytes
+  void* v_cache;
+  const int64_t* slot_mapping;  // [T]
+  int64_t k_stride_bytes, v_stride_bytes;
+  int64_t num_slots;        // num_pages * page_size
+  int T;
+  int row_bytes;            // H_kv * d * element size
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
+hipError_t launch_store_kvcache(const StoreParams& p, hipStream_t s);
 
 // Wavefronts per workgroup of the bf16 forward kernel; each owns 32 query rows.
 #ifndef ATTN_FWD_NW

@@ -1,8 +1,9 @@
 /*
  * attn.h — C ABI of libattn.so: exact attention forward for AMD Instinct MI355X (gfx950).
  *
- * Three entry points, one per way the attention library is called on the
- * dlog.com.cn page "From standard Attention to FlashAttention and paged execution":
+ * Three attention entry points, one per way the attention library is called on the
+ * dlog.com.cn page "From standard Attention to FlashAttention and paged execution",
+ * and the KV-cache write that precedes them (attn_store_kvcache):
  *
  *   attn_fwd            fixed-length batched attention (section 3.1, the basic
  *                       fixed-length interface), layout [B, H, N, d] by default;
@@ -10,7 +11,9 @@
  *                       sequence lengths (section 3.3, cu_seqlens);
  *   attn_decode_paged   one new query token per sequence attending its cached
  *                       K/V, read page by page through a block table
- *                       (sections 3.4 and "PagedAttention").
+ *                       (sections 3.4 and "PagedAttention");
+ *   attn_store_kvcache  the step's new K/V rows written into the page pools
+ *                       through slot_mapping.
  *
  * Each computes, per query row i, O_i = sum_j softmax_j(scale * q_i . k_j) v_j over
  * the admissible keys j, and the row's logsumexp lse_i = ln sum_j exp(scale * q_i . k_j)
@@ -128,6 +131,31 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
                       const int32_t* context_lens, int B, int num_pages, int page_size,
                       int H, int H_kv, int d, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_store_kvcache — write one step's new K/V rows into the paged pools.
+ *
+ * The engine's attention step on the dlog.com.cn page first stores the step's k/v into
+ * the paged KV cache through slot_mapping (prefill: a batch of new tokens; decode: one
+ * token per sequence), then runs attention over the pools.
+ *
+ * k, v : token-major rows; token t's [H_kv, d] row starts at element t * k_token_stride
+ *        (v_token_stride) and is contiguous.  Strides >= H_kv * d, so the K and V parts of
+ *        a fused [T, (H + 2 H_kv) * d] projection output are accepted without copies.
+ * slot_mapping : int64 [T] device array; token t's row goes to pool slot
+ *        slot_mapping[t] = page * page_size + offset (block_table[b][i] = page holds
+ *        tokens i * page_size ... of sequence b).  Slots outside [0, num_pages *
+ *        page_size), -1 for padding among them, are skipped: nothing is written for them.
+ *        Two tokens naming the same slot is a caller error (which row lands is not
+ *        specified).
+ * k_cache, v_cache : [num_pages, page_size, H_kv, d] contiguous pools, written in place.
+ * dtype : ATTN_DTYPE_BF16 or ATTN_DTYPE_F32 (a byte copy; rows and strides must be
+ *        multiples of 16 bytes, else ATTN_ERR_UNSUPPORTED).
+ */
+int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int T, int H_kv, int d,
+                       int64_t k_token_stride, int64_t v_token_stride,
+                       int num_pages, int page_size, int dtype, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

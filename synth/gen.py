@@ -243,6 +243,57 @@ def paged(B: int = 64, H: int = 32, d: int = 128, ctx_min: int = 512, ctx_max: i
                  ctx.astype(np.int32), bt, num_pages, q, kc, vc)
 
 
+@dataclass
+class KVStore:
+    """New K/V rows [T, H_kv, d] (bf16 bits) to be written into pools [P, page, H_kv, d]
+    through slot_mapping int64 [T] (slot = page * page_size + offset, -1 = padding)."""
+    T: int
+    H_kv: int
+    d: int
+    page: int
+    num_pages: int
+    k: np.ndarray
+    v: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    slot_mapping: np.ndarray
+
+
+def kvstore(lens, H_kv: int = 32, d: int = 128, page: int = 16, extra_pages: int = 0, pad: int = 0,
+            seed: int = 0) -> KVStore:
+    """Tokens of sequences with lengths ``lens`` laid out page by page: draw order is
+    the page permutation rng.permutation(num_pages) dealt out to sequences in order
+    (as for the decode pools), then ``pad`` padding positions rng.choice(T + pad, pad)
+    whose slot is -1, then K, V and the two pools (random bits of the old contents)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    pages_b = (lens + page - 1) // page
+    used = int(pages_b.sum())
+    num_pages = used + extra_pages
+    perm = rng.permutation(num_pages)
+    slots = []
+    off = 0
+    for L, n in zip(lens, pages_b):
+        pg = perm[off:off + int(n)]
+        off += int(n)
+        t = np.arange(int(L))
+        slots.append(pg[t // page] * page + t % page)
+    slots = np.concatenate(slots) if slots else np.zeros(0, dtype=np.int64)
+    T = len(slots) + pad
+    if pad:
+        where = np.sort(rng.choice(T, size=pad, replace=False))
+        full = np.full(T, -1, dtype=np.int64)
+        keep = np.ones(T, dtype=bool)
+        keep[where] = False
+        full[keep] = slots
+        slots = full
+    k = normal(seed, T_K, (T, H_kv, d), True)
+    v = normal(seed, T_V, (T, H_kv, d), True)
+    kc = normal(seed, T_KCACHE, (num_pages, page, H_kv, d), True)
+    vc = normal(seed, T_VCACHE, (num_pages, page, H_kv, d), True)
+    return KVStore(T, H_kv, d, page, num_pages, k, v, kc, vc, slots.astype(np.int64))
+
+
 # --------------------------------------------------------------------------- named workloads
 
 HAND_Q = np.array([[1, 0, 2], [0, 1, 1]], dtype=np.float32)
@@ -257,6 +308,8 @@ WORKLOADS = {
     "c5": "paged decode bf16 64 seqs ctx U[512,8192] H=32 d=128 page 16",
     "gqa_decode": "paged decode bf16 64 seqs ctx U[512,8192] H=16 H_kv=8 d=128 page 16 "
                   "(the page's 16-query-head / 8-KV-head model shape)",
+    "store_prefill": "store_kvcache of a prefill batch: the 16 varlen lengths (34069 tokens), "
+                     "H_kv=32 d=128 bf16, 16-token pages in a random page order",
 }
 
 
@@ -273,4 +326,7 @@ def workload(name: str, seed: int = 0, **kw):
         return paged(64, 32, 128, 512, 8192, 16, seed=seed, **kw)
     if name == "gqa_decode":
         return paged(64, 16, 128, 512, 8192, 16, seed=seed, H_kv=8, **kw)
+    if name == "store_prefill":
+        lens = np.random.default_rng(seed).integers(128, 4096, size=16, endpoint=True)
+        return kvstore(lens, 32, 128, 16, seed=seed)
     raise KeyError(name)

@@ -149,3 +149,28 @@ def test_status_strings():
     assert attn.status_string(0) == "ok"
     assert "unsupported" in attn.status_string(2)
     assert attn.status_string(99) == "unknown status"
+
+
+def store(**kw):
+    a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=16, Hkv=8, d=128, ks=8 * 128, vs=8 * 128,
+             P=32, page=16, dtype=attn.ATTN_DTYPE_BF16)
+    a.update(kw)
+    return attn.load().attn_store_kvcache(a["k"], a["v"], a["kc"], a["vc"], a["slots"], a["T"], a["Hkv"], a["d"],
+                                          a["ks"], a["vs"], a["P"], a["page"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(T=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(slots=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(kc=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ks=8 * 128 - 8), attn.ATTN_ERR_INVALID_ARG),    # rows would overlap
+    (dict(ks=8 * 128 + 4), attn.ATTN_ERR_UNSUPPORTED),    # 8-byte aligned only
+    (dict(Hkv=1, d=4, ks=4, vs=4), attn.ATTN_ERR_UNSUPPORTED),   # 8-byte rows
+    (dict(k=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(slots=ctypes.c_void_p((1 << 20) + 4)), attn.ATTN_ERR_INVALID_ARG),
+    (dict(T=0), attn.ATTN_OK),
+    (dict(P=0), attn.ATTN_OK),
+])
+def test_store_kvcache_rejects_before_launch(kw, status):
+    assert store(**kw) == status

@@ -371,3 +371,77 @@ def test_gqa_decode_full_sampled(A):
                                            heads=[0, 1, 7, 14, 15])
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+# ------------------------------------------------------------------ store_kvcache (bit-exact)
+
+def _bits(t):
+    """Device tensor -> host uint16 bit patterns (bf16) or uint32 (fp32)."""
+    import torch
+    h = t.detach().cpu().contiguous()
+    return h.view(torch.int16).numpy().view(np.uint16) if h.dtype == torch.bfloat16 else h.view(torch.int32).numpy().view(np.uint32)
+
+
+def _store_and_compare(A, w, k=None, v=None):
+    import torch
+    kd = dev(w.k) if k is None else k
+    vd = dev(w.v) if v is None else v
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    A.attn_store_kvcache(kd, vd, kc, vc, torch.from_numpy(w.slot_mapping).cuda())
+    torch.cuda.synchronize()
+    ek, ev = oracle.store_kvcache(w.k, w.v, w.k_cache, w.v_cache, w.slot_mapping)
+    assert np.array_equal(_bits(kc), ek), "k_cache differs"
+    assert np.array_equal(_bits(vc), ev), "v_cache differs"
+
+
+@pytest.mark.parametrize("lens,Hkv,d,pad,extra", [
+    ([1], 1, 64, 0, 0),
+    ([5, 17, 3, 40], 2, 128, 3, 2),
+    ([64] * 8, 8, 128, 0, 4),               # decode-like: whole pages
+    ([300, 1, 77], 8, 64, 20, 1),
+])
+def test_store_kvcache_bitexact(A, lens, Hkv, d, pad, extra):
+    w = synth.kvstore(lens, Hkv, d, 16, extra_pages=extra, pad=pad, seed=50)
+    _store_and_compare(A, w)
+
+
+def test_store_kvcache_out_of_pool_slots_skipped(A):
+    w = synth.kvstore([20, 9], 2, 64, 16, extra_pages=1, seed=51)
+    w.slot_mapping[3] = w.num_pages * 16          # one past the pool
+    w.slot_mapping[7] = 1 << 40
+    w.slot_mapping[11] = -5
+    _store_and_compare(A, w)
+
+
+def test_store_kvcache_fused_qkv_slices(A):
+    """K and V read as strided slices of a fused [T, (H + 2 H_kv) d] projection output."""
+    import torch
+    H, Hkv, d = 8, 2, 128
+    w = synth.kvstore([33, 100], Hkv, d, 16, seed=52)
+    q = synth.normal(52, synth.T_Q, (w.T, H, d), True)
+    fused = np.concatenate([q.reshape(w.T, -1), w.k.reshape(w.T, -1), w.v.reshape(w.T, -1)], axis=1)
+    f = dev(fused)
+    k = f[:, H * d:(H + Hkv) * d].view(w.T, Hkv, d)
+    v = f[:, (H + Hkv) * d:].view(w.T, Hkv, d)
+    assert k.stride(0) == (H + 2 * Hkv) * d
+    _store_and_compare(A, w, k, v)
+
+
+def test_store_kvcache_fp32(A):
+    import torch
+    w = synth.kvstore([21, 5], 2, 64, 16, pad=2, seed=53)
+    as32 = lambda b: oracle.bf16_bits_to_f64(b).astype(np.float32)
+    k, v, kc0, vc0 = as32(w.k), as32(w.v), as32(w.k_cache), as32(w.v_cache)
+    kc, vc = torch.from_numpy(kc0).cuda(), torch.from_numpy(vc0).cuda()
+    A.attn_store_kvcache(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), kc, vc,
+                         torch.from_numpy(w.slot_mapping).cuda())
+    torch.cuda.synchronize()
+    ek, ev = oracle.store_kvcache(k, v, kc0, vc0, w.slot_mapping)
+    assert np.array_equal(kc.cpu().numpy().view(np.uint32), ek.view(np.uint32))
+    assert np.array_equal(vc.cpu().numpy().view(np.uint32), ev.view(np.uint32))
+
+
+def test_store_kvcache_full_prefill(A):
+    """The prefill store the bench times: 34069 tokens, 32 KV heads, d = 128, every slot."""
+    w = synth.workload("store_prefill")
+    _store_and_compare(A, w)
