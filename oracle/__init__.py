@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
     attention_rows,
     attention_dense,
     attention_varlen,
+    attention_varlen_paged,
     attention_decode_paged,
     gather_paged,
     kv_head,

@@ -216,3 +216,40 @@ def store_kvcache(k, v, k_cache, v_cache, slot_mapping):
             kc[slot // page, slot % page] = k[t]
             vc[slot // page, slot % page] = v[t]
     return kc, vc
+
+
+def attention_varlen_paged(q, k_cache, v_cache, cu_q, cu_k, block_table, scale: float,
+                           causal: bool = False, seqs=None, heads=None, rows_per_seq=None):
+    """Variable-length attention whose keys and values live in the paged pools (paged
+    prefill: "From standard Attention to FlashAttention and paged execution", the
+    prefill entry of the v3 engine: a continued chunk passes the KV cache and its
+    block_table to the varlen function, with cu_seqlens_q != cu_seqlens_k).
+    Sequence s has Lq = cu_q[s+1] - cu_q[s] new query rows and Lk = cu_k[s+1] - cu_k[s]
+    keys; key j is token j of the sequence, in page block_table[s][j // page], slot
+    j % page (the pools [pages, page, H_kv, d]).  Under the causal mask the query rows
+    are the last Lq tokens (bottom-right).  Returns O [total_q, H, d], lse [total_q, H]."""
+    tq, H, d = q.shape
+    H_kv = k_cache.shape[2]
+    page = k_cache.shape[1]
+    dv = v_cache.shape[3]
+    o = np.full((tq, H, dv), np.nan)
+    lse = np.full((tq, H), np.nan)
+    S = len(cu_q) - 1
+    seqs = range(S) if seqs is None else seqs
+    heads = range(H) if heads is None else heads
+    for s in seqs:
+        q0, q1 = int(cu_q[s]), int(cu_q[s + 1])
+        lk = int(cu_k[s + 1]) - int(cu_k[s])
+        rows = None
+        if rows_per_seq is not None:
+            rows = np.asarray(rows_per_seq(s, q1 - q0), dtype=np.int64)
+        for h in heads:
+            hk = kv_head(h, H, H_kv)
+            kb = gather_paged(k_cache[:, :, hk], block_table[s], lk, page)
+            vb = gather_paged(v_cache[:, :, hk], block_table[s], lk, page)
+            ob, lb = attention_rows(q[q0:q1, h], kb, vb, scale, causal, rows=rows)
+            if rows is None:
+                o[q0:q1, h], lse[q0:q1, h] = ob, lb
+            else:
+                o[q0 + rows, h], lse[q0 + rows, h] = ob, lb
+    return o, lse

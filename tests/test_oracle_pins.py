@@ -468,3 +468,54 @@ def test_store_kvcache_skips_padding_and_out_of_range_slots():
     assert np.array_equal(kc, expect_k)
     assert np.array_equal(vc[0, 3], v[2]) and np.array_equal(np.delete(vc.reshape(8, 1, 2), 3, 0),
                                                               np.delete(vc0.reshape(8, 1, 2), 3, 0))
+
+
+# ----------------------------------------------------------------- paged prefill
+
+def _pages_for(lens, page, r, extra=1):
+    n = [(L + page - 1) // page for L in lens]
+    P = sum(n) + extra
+    perm = r.permutation(P)
+    bt = np.full((len(lens), max(n)), P - 1, dtype=np.int32)
+    off = 0
+    for s, m in enumerate(n):
+        bt[s, :m] = perm[off:off + m]
+        off += m
+    return bt, P
+
+
+def test_paged_prefill_brute_force_gather():
+    """Keys gathered token by token through the block table; query rows are the last
+    Lq tokens (bottom-right causal), e.g. a continued chunk after a cached prefix."""
+    r = rng(60)
+    page, H, Hkv, d = 4, 4, 2, 3
+    lq, lk = [2, 5, 1], [9, 5, 6]
+    bt, P = _pages_for(lk, page, r)
+    kc, vc = r.normal(size=(P, page, Hkv, d)), r.normal(size=(P, page, Hkv, d))
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = r.normal(size=(cq[-1], H, d))
+    for causal in (False, True):
+        o, l = oracle.attention_varlen_paged(q, kc, vc, cq, ck, bt, 0.9, causal)
+        for s in range(3):
+            for h in range(H):
+                hk = h // (H // Hkv)
+                ks = [kc[bt[s, t // page], t % page, hk].tolist() for t in range(lk[s])]
+                vs = [vc[bt[s, t // page], t % page, hk].tolist() for t in range(lk[s])]
+                ob, lb = _brute(q[cq[s]:cq[s + 1], h].tolist(), ks, vs, 0.9, causal)
+                assert np.abs(o[cq[s]:cq[s + 1], h] - ob).max() < TIGHT
+                assert np.abs(l[cq[s]:cq[s + 1], h] - lb).max() < TIGHT
+
+
+def test_paged_prefill_last_row_is_decode():
+    """With one new query token per sequence, paged prefill is the paged decode."""
+    r = rng(61)
+    page, H, d = 4, 2, 3
+    lk = [7, 12]
+    bt, P = _pages_for(lk, page, r)
+    kc, vc = r.normal(size=(P, page, H, d)), r.normal(size=(P, page, H, d))
+    q = r.normal(size=(2, H, d))
+    o, l = oracle.attention_varlen_paged(q, kc, vc, np.array([0, 1, 2]), np.concatenate([[0], np.cumsum(lk)]),
+                                         bt, 0.5, True)
+    od, ld = oracle.attention_decode_paged(q, kc, vc, bt, np.array(lk), 0.5)
+    assert np.abs(o - od).max() < TIGHT and np.abs(l - ld).max() < TIGHT
