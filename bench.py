@@ -8,6 +8,8 @@ One step = one call of each entry point on its workload, inputs resident in HBM:
                      (headline, HBM GB/s)
   attn_decode_paged  the same lengths with 16 query heads on 8 KV heads (grouped-query)
   attn_store_kvcache the varlen batch's 34069 new K/V rows written into 16-token pages
+  attn_fwd_varlen    paged prefill: the second half of each of those sequences as new
+                     causal rows over its whole context, read through the block table
 
 W untimed warm-up steps, then K timed steps; every kernel call is bracketed by HIP
 events on the stream it runs on.  Prints ONE JSON line.  `value` is the dense
@@ -110,7 +112,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache"], default=None,
+    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache", "prefill_paged"],
+                    default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
@@ -164,6 +167,14 @@ def main() -> int:
     w6.k_cache = w6.v_cache = None
     log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
 
+    w8 = synth.workload("prefill_paged")
+    q8, kc8, vc8 = dev(w8.q), dev(w8.k_cache), dev(w8.v_cache)
+    cq8, ck8, bt8 = dev(w8.cu_q), dev(w8.cu_k), dev(w8.block_table)
+    o8 = torch.empty_like(q8)
+    l8 = torch.empty((q8.shape[0], 32), dtype=torch.float32, device="cuda")
+    w8.k_cache = w8.v_cache = None
+    log(f"[bench] paged prefill workload ready ({time.perf_counter() - t:.1f} s)")
+
     w7 = synth.workload("store_prefill")
     k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
     sl7 = torch.from_numpy(w7.slot_mapping).cuda()
@@ -184,8 +195,12 @@ def main() -> int:
     def run_store():
         attn.attn_store_kvcache(k7, v7, kc7, vc7, sl7)
 
+    def run_prefill_paged():
+        attn.attn_fwd_varlen(q8, kc8, vc8, cq8, ck8, w8.max_q, w8.max_k, scale=w8.scale, causal=True,
+                             out=o8, lse=l8, block_table=bt8)
+
     parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa),
-             ("store_kvcache", run_store)]
+             ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged)]
     if args.only:
         parts = [p for p in parts if p[0] == args.only]
 
@@ -251,6 +266,14 @@ def main() -> int:
                              "ms": ms["decode_gqa"].mean(), "GB/s": by6 / t6 / 1e9, "peak": PEAK_HBM_GBS,
                              "frac": by6 / t6 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by6,
                              "note": "KV bytes counted once per KV head (grouped-query)"}
+    if "prefill_paged" in ms:
+        t8 = ms["prefill_paged"].mean() / 1e3
+        lq8, lk8 = w8.lens_q.astype(np.float64), w8.lens_k.astype(np.float64)
+        fl8 = float(np.sum(4.0 * 128 * 32 * (lq8 * (lk8 - lq8) + lq8 * (lq8 + 1) / 2)))  # admissible pairs x 4d
+        res["prefill_paged"] = {"workload": f"16 seqs, {int(lq8.sum())} new causal rows over {int(lk8.sum())} "
+                                            "context tokens in 16-token pages, H=32 d=128 bf16",
+                                "ms": ms["prefill_paged"].mean(), "tflops": fl8 / t8 / 1e12,
+                                "frac": fl8 / t8 / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": fl8}
     if "store_kvcache" in ms:
         t7 = ms["store_kvcache"].mean() / 1e3
         by7 = 4 * w7.T * w7.H_kv * w7.d * 2 + 8 * w7.T   # K and V read and written once, slots read

@@ -40,7 +40,8 @@ def load() -> ctypes.CDLL:
     vp, i32, i64p, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64p, i64p, i64p, i64p, f32, i32, vp]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    vp, i32, i32, f32, i32, vp]
     lib.attn_fwd_varlen.restype = i32
     lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_paged_workspace_size.restype = sz
@@ -123,16 +124,27 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                     scale: float | None = None, causal: bool = False, out=None, lse=None,
-                    with_lse: bool = True, stream=None):
-    """Packed variable-length attention.  q [total_q, H, d], k/v [total_k, H_kv, d]
-    contiguous bf16 (H_kv divides H); cu_seqlens_* int32 device tensors
-    [num_seqs + 1].  Returns (o [total_q, H, d], lse float32 [total_q, H])."""
+                    with_lse: bool = True, stream=None, block_table=None):
+    """Packed variable-length attention.  q [total_q, H, d]; k/v [total_k, H_kv, d]
+    contiguous bf16 (H_kv divides H), or with ``block_table`` (int32 [num_seqs,
+    max_pages]) the page pools [num_pages, page, H_kv, d] (paged prefill);
+    cu_seqlens_* int32 device tensors [num_seqs + 1].  Returns (o [total_q, H, d],
+    lse float32 [total_q, H])."""
     torch = _torch()
     lib = load()
     tq, H, d = q.shape
-    Hkv = k.shape[1]
-    if k.shape[2] != d or v.shape != k.shape:
-        raise ValueError("k and v must be [total_k, H_kv, d] matching q")
+    if block_table is None:
+        Hkv = k.shape[1]
+        if k.shape[2] != d or v.shape != k.shape:
+            raise ValueError("k and v must be [total_k, H_kv, d] matching q")
+        bt, maxp, page = None, 0, 0
+    else:
+        Hkv, page = k.shape[2], k.shape[1]
+        if k.dim() != 4 or k.shape[3] != d or v.shape != k.shape:
+            raise ValueError("paged k and v must be [num_pages, page, H_kv, d] matching q")
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous int32 tensor")
+        bt, maxp = block_table, block_table.shape[1]
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("varlen tensors must be contiguous [tokens, H, d]")
@@ -147,8 +159,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         lse = torch.empty((tq, H), dtype=torch.float32, device=q.device)
     rc = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if with_lse else None,
                              _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q),
-                             int(max_seqlen_k), H, Hkv, d, _dtype_code(q), scale, int(bool(causal)),
-                             _stream(stream))
+                             int(max_seqlen_k), H, Hkv, d, _dtype_code(q), _ptr(bt), maxp, page, scale,
+                             int(bool(causal)), _stream(stream))
     _check(rc, "attn_fwd_varlen")
     return o, (lse if with_lse else None)
 

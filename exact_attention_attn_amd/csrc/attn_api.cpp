@@ -119,6 +119,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                     int max_seqlen_q, int max_seqlen_k, int H, int H_kv, int d, int dtype,
+                    const int32_t* block_table, int max_pages_per_seq, int page_size,
                     float scale, int causal, void* stream) {
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || H < 0) return fail(ATTN_ERR_INVALID_ARG);
   if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
@@ -132,9 +133,19 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   if (!aligned16(q) || !aligned16(o) || (max_seqlen_k > 0 && (!aligned16(k) || !aligned16(v))))
     return fail(ATTN_ERR_UNSUPPORTED);
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  int page_shift = 0;
+  if (block_table != nullptr) {  // paged K/V: page size a power of two, at least 16
+    if (page_size < 16 || (page_size & (page_size - 1)) != 0) return fail(ATTN_ERR_UNSUPPORTED);
+    if (max_pages_per_seq < 0 || (int64_t)max_pages_per_seq * page_size < max_seqlen_k)
+      return fail(ATTN_ERR_INVALID_ARG);
+    while ((1 << page_shift) < page_size) ++page_shift;
+  }
 
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.block_table = block_table;
+  p.bt_stride = max_pages_per_seq;
+  p.page_shift = page_shift;
   const int64_t tok = (int64_t)H * d, ktok = (int64_t)H_kv * d;
   p.q_sn = tok; p.q_sh = d;
   p.k_sn = ktok; p.k_sh = d;

@@ -85,7 +85,9 @@ __device__ __forceinline__ void block_coords(const FwdParams& p, int& rb, int& b
   rb = CAUSAL ? (p.n_rb - 1 - rbi) : rbi;
 }
 
-template <bool VARLEN>
+// Per-(sequence, head) extents and element offsets.  Paged K/V: koff / voff only select
+// the KV head inside a slot; the page comes from the block table per key.
+template <bool VARLEN, bool PAGED = false>
 __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int h, int& Lq, int& Lk,
                                            int64_t& qoff, int64_t& koff, int64_t& voff,
                                            int64_t& ooff, int64_t& loff) {
@@ -96,8 +98,8 @@ __device__ __forceinline__ void seq_bounds(const FwdParams& p, int b, int h, int
     Lq = q1 - q0;
     Lk = k1 - k0;
     qoff = (int64_t)q0 * p.q_sn + (int64_t)h * p.q_sh;
-    koff = (int64_t)k0 * p.k_sn + (int64_t)hk * p.k_sh;
-    voff = (int64_t)k0 * p.v_sn + (int64_t)hk * p.v_sh;
+    koff = (PAGED ? 0 : (int64_t)k0 * p.k_sn) + (int64_t)hk * p.k_sh;
+    voff = (PAGED ? 0 : (int64_t)k0 * p.v_sn) + (int64_t)hk * p.v_sh;
     ooff = (int64_t)q0 * p.o_sn + (int64_t)h * p.o_sh;
     loff = (int64_t)q0 * p.l_sn + (int64_t)h * p.l_sh;
   } else {
@@ -159,7 +161,19 @@ __device__ __forceinline__ void dma16(u32x4s r, const uint8_t* lds, int voffset)
                : "memory", "m0");
 }
 
-template <int D, int NW, int BN, bool CAUSAL, bool VARLEN>
+// Same, from a per-lane 64-bit address (global_load_lds): the gather of paged K/V, whose
+// rows may lie anywhere in pools larger than a buffer resource's 32-bit offsets reach.
+// The address must be valid: paged keys past a sequence's end are clamped to its last
+// key, so only block-table entries of the sequence's own pages are used.
+__device__ __forceinline__ void dma16g(const void* src, const uint8_t* lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(src)
+               : "memory", "m0");
+}
+
+template <int D, int NW, int BN, bool CAUSAL, bool VARLEN, bool PAGED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ATTN_FWD_WPE, ATTN_FWD_WPE))) fwd_bf16_kernel(const FwdParams p) {
   constexpr int BM = 32 * NW;       // query rows per workgroup
   constexpr int NS = BN / 32;       // 32-key blocks per key tile
@@ -193,7 +207,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
   block_coords<CAUSAL>(p, rb, b, h);
   int Lq, Lk;
   int64_t qoff, koff, voff, ooff, loff;
-  seq_bounds<VARLEN>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
+  seq_bounds<VARLEN, PAGED>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
   const int row0 = rb * BM;
   if (row0 >= Lq) return;  // uniform over the workgroup
 
@@ -244,7 +258,35 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
     vdoff[i] = vkey[i] * vrow_bytes + vcol[i];
   }
 
+  // Paged K/V: the physical page of each lane's key in the K (V) tile about to be loaded,
+  // fetched from the block table one step before its load is issued.
+  const int32_t* __restrict__ bt_row = PAGED ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
+  const int pshift = PAGED ? p.page_shift : 0;
+  const int pmask = (1 << pshift) - 1;
+  int kpg[PAGED ? BPW : 1], vpg[PAGED ? BPW : 1];
+  auto load_pages = [&](int j, const int* key, int* pg) {
+    const int kt0 = j * BN;
+    const int last = Lk - kt0 - 1;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) pg[i] = bt_row[(kt0 + min(key[i], last)) >> pshift];
+  };
+  auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* key, const int* colb,
+                         const int* pg, int row_bytes) {
+    const int kt0 = j * BN;
+    const int last = Lk - kt0 - 1;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int tok = kt0 + min(key[i], last);
+      const int64_t slot = ((int64_t)pg[i] << pshift) + (tok & pmask);
+      dma16g((const uint8_t*)base + slot * row_bytes + colb[i], buf + (wave * BPW + i) * 1024);
+    }
+  };
+
   auto issue_k = [&](int j, uint8_t* kb) {
+    if (PAGED) {
+      issue_paged(j, kb, Kg, kkey, kcol, kpg, krow_bytes);
+      return;
+    }
     const int kt0 = j * BN;
     const int last = Lk - kt0 - 1;  // last valid row of this tile (>= 0)
     const int64_t krem = ((int64_t)last * ksn + D) * 2;  // bytes of valid keys from kt0 on
@@ -259,6 +301,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
     }
   };
   auto issue_v = [&](int j, uint8_t* vb) {
+    if (PAGED) {
+      issue_paged(j, vb, Vg, vkey, vcol, vpg, vrow_bytes);
+      return;
+    }
     const int kt0 = j * BN;
     const int last = Lk - kt0 - 1;
     const int64_t vrem = ((int64_t)last * vsn + D) * 2;
@@ -309,9 +355,20 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
 
   if (ntiles > 0) {
     // prologue: K0, V0, K1 in flight; S_0 and its row max
+    if (PAGED) {
+      load_pages(0, kkey, kpg);
+      load_pages(0, vkey, vpg);
+    }
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
-    if (ntiles > 1) issue_k(1, kbuf1);
+    if (ntiles > 1) {
+      if (PAGED) load_pages(1, kkey, kpg);
+      issue_k(1, kbuf1);
+    }
+    if (PAGED) {  // pages of the first step's loads: K_2 and V_1
+      if (ntiles > 2) load_pages(2, kkey, kpg);
+      if (ntiles > 1) load_pages(1, vkey, vpg);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 sA[NS], sB[NS];  // S of the current and the next tile, alternating roles
@@ -359,6 +416,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
         for (int c = 0; c < NS; ++c) a[u][c] = kop(kcur, u, c);
       if (j + 2 < ntiles) issue_k(j + 2, kdma);
       if (j + 1 < ntiles) issue_v(j + 1, vdma);
+      if (PAGED) {  // pages of the next step's loads, landing with this step's tiles
+        if (j + 3 < ntiles) load_pages(j + 3, kkey, kpg);
+        if (j + 2 < ntiles) load_pages(j + 2, vkey, vpg);
+      }
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {      // deferred rescale (rare)
         const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
         l *= alpha;
@@ -564,7 +625,10 @@ hipError_t launch_bf16_t(const FwdParams& p, hipStream_t s) {
   constexpr int NW = kFwdNW;
   const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
   if (nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, CAUSAL, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+  if (VARLEN && p.block_table != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, CAUSAL, VARLEN, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, CAUSAL, VARLEN, false>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -31,6 +31,12 @@ struct FwdParams {
   int Nk;     // dense: key length;   varlen: max_seqlen_k
   int n_rb;   // query row blocks per (b, h)
   int kv_group;  // query heads per KV head (1: multi-head attention)
+  // Paged K/V (varlen only): sequence b's key j is slot j & (2^page_shift - 1) of page
+  // block_table[b * bt_stride + (j >> page_shift)]; k/v point at the pools and the
+  // token stride k_sn / v_sn is the slot stride.  block_table == nullptr: contiguous.
+  const int32_t* block_table;
+  int bt_stride;
+  int page_shift;
   float scale_log2;  // scale * log2(e): scores are handled in base-2 units
 };
 
@@ -67,7 +73,7 @@ struct StoreParams {
 };
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);  // paged iff p.block_table
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_store_kvcache(const StoreParams& p, hipStream_t s);

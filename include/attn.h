@@ -87,20 +87,32 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              float scale, int causal, void* stream);
 
 /*
- * attn_fwd_varlen — packed variable-length batch (bfloat16).
+ * attn_fwd_varlen — packed variable-length batch (bfloat16), keys contiguous or paged.
  *
- * q, o : [total_q, H, d] contiguous;  k, v : [total_k, H_kv, d] contiguous.
+ * q, o : [total_q, H, d] contiguous;  k, v : [total_k, H_kv, d] contiguous, or, when
+ *        block_table is not NULL, the page pools [num_pages, page_size, H_kv, d].
  * cu_seqlens_q, cu_seqlens_k : int32 [num_seqs + 1] device arrays of prefix sums;
  *        sequence s owns Q rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and K/V rows
  *        [cu_seqlens_k[s], cu_seqlens_k[s+1]) (the page's example [0, 3, 7] is two
  *        sequences of 3 and 4 tokens).  Sequences never attend to each other.
  * max_seqlen_q / max_seqlen_k : upper bounds of the per-sequence lengths (they size
  *        the launch grid; a smaller value than the truth is a contract violation).
+ * block_table, max_pages_per_seq, page_size : paged prefill (the page's v3 prefill
+ *        entry continuing a chunk on the KV cache).  NULL block_table: contiguous K/V
+ *        and the other two are ignored.  Otherwise sequence s's key j is slot
+ *        j % page_size of page block_table[s * max_pages_per_seq + j / page_size];
+ *        only cu_seqlens_k's differences (the key counts) are used; cu_seqlens_q may
+ *        differ from cu_seqlens_k, and under the causal mask the query rows are the
+ *        sequence's last tokens (bottom-right).  page_size must be a power of two
+ *        >= 16 (else ATTN_ERR_UNSUPPORTED) and max_pages_per_seq * page_size >=
+ *        max_seqlen_k (else ATTN_ERR_INVALID_ARG).  Every block-table entry a sequence
+ *        uses must name a page of the pools (the pages are gathered by address).
  * lse  : float32 [total_q, H], or NULL.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int num_seqs,
                     int max_seqlen_q, int max_seqlen_k, int H, int H_kv, int d, int dtype,
+                    const int32_t* block_table, int max_pages_per_seq, int page_size,
                     float scale, int causal, void* stream);
 
 /*

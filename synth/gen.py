@@ -244,6 +244,73 @@ def paged(B: int = 64, H: int = 32, d: int = 128, ctx_min: int = 512, ctx_max: i
 
 
 @dataclass
+class PagedPrefill:
+    """Paged prefill: new query rows q [sum(lens_q), H, d] of sequences whose keys (the
+    cached prefix and the new tokens, lens_k in all) sit in pools [num_pages + 1, page,
+    H_kv, d] through block_table [S, max_pages] (padded with the poison page
+    num_pages).  Values are bf16 bits."""
+    H: int
+    H_kv: int
+    d: int
+    page: int
+    causal: bool
+    scale: float
+    lens_q: np.ndarray
+    lens_k: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    block_table: np.ndarray
+    num_pages: int
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+
+    @property
+    def max_q(self) -> int:
+        return int(self.lens_q.max()) if len(self.lens_q) else 0
+
+    @property
+    def max_k(self) -> int:
+        return int(self.lens_k.max()) if len(self.lens_k) else 0
+
+
+def paged_prefill(lens_q, lens_k, H: int = 32, d: int = 128, page: int = 16, causal: bool = True,
+                  scale: float | None = None, seed: int = 0, H_kv: int | None = None,
+                  poison: bool = True) -> PagedPrefill:
+    """Draw order: the page permutation rng.permutation(num_pages) dealt out to the
+    sequences in order, then q, k_cache, v_cache.  With ``poison`` the padding page and
+    the slots past each sequence's last key are NaN (a kernel that reads them fails)."""
+    H_kv = H if H_kv is None else H_kv
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = np.asarray(lens_k, dtype=np.int64)
+    pages_b = (lens_k + page - 1) // page
+    num_pages = int(pages_b.sum())
+    perm = rng.permutation(num_pages)
+    maxp = max(1, int(pages_b.max()) if len(pages_b) else 1)
+    bt = np.full((len(lens_k), maxp), num_pages, dtype=np.int32)
+    off = 0
+    for s_, n in enumerate(pages_b):
+        bt[s_, :int(n)] = perm[off:off + int(n)]
+        off += int(n)
+    cu_q, cu_k = cu_from_lens(lens_q), cu_from_lens(lens_k)
+    q = normal(seed, T_Q, (int(cu_q[-1]), H, d), True)
+    kc = normal(seed, T_KCACHE, (num_pages + 1, page, H_kv, d), True)
+    vc = normal(seed, T_VCACHE, (num_pages + 1, page, H_kv, d), True)
+    if poison:
+        kc[num_pages] = BF16_NAN
+        vc[num_pages] = BF16_NAN
+        for s_, L in enumerate(lens_k):
+            tail = int(L % page)
+            if tail:
+                pg = int(bt[s_, pages_b[s_] - 1])
+                kc[pg, tail:] = BF16_NAN
+                vc[pg, tail:] = BF16_NAN
+    return PagedPrefill(H, H_kv, d, page, causal, 1.0 / math.sqrt(d) if scale is None else scale,
+                        lens_q, lens_k, cu_q, cu_k, bt, num_pages, q, kc, vc)
+
+
+@dataclass
 class KVStore:
     """New K/V rows [T, H_kv, d] (bf16 bits) to be written into pools [P, page, H_kv, d]
     through slot_mapping int64 [T] (slot = page * page_size + offset, -1 = padding)."""
@@ -310,6 +377,8 @@ WORKLOADS = {
                   "(the page's 16-query-head / 8-KV-head model shape)",
     "store_prefill": "store_kvcache of a prefill batch: the 16 varlen lengths (34069 tokens), "
                      "H_kv=32 d=128 bf16, 16-token pages in a random page order",
+    "prefill_paged": "paged prefill: the 16 varlen lengths as contexts in 16-token pages, the "
+                     "second half of each (ceil(L/2) tokens) as new causal query rows, H=32 d=128",
 }
 
 
@@ -326,6 +395,9 @@ def workload(name: str, seed: int = 0, **kw):
         return paged(64, 32, 128, 512, 8192, 16, seed=seed, **kw)
     if name == "gqa_decode":
         return paged(64, 16, 128, 512, 8192, 16, seed=seed, H_kv=8, **kw)
+    if name == "prefill_paged":
+        lens = np.random.default_rng(seed).integers(128, 4096, size=16, endpoint=True)
+        return paged_prefill((lens + 1) // 2, lens, 32, 128, 16, True, seed=seed, **kw)
     if name == "store_prefill":
         lens = np.random.default_rng(seed).integers(128, 4096, size=16, endpoint=True)
         return kvstore(lens, 32, 128, 16, seed=seed)

@@ -79,11 +79,11 @@ def test_fwd_rejects_before_launch(kw, status):
 
 def varlen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cq=FAKE, ck=FAKE, S=2, mq=16, mk=16, H=2, Hkv=2, d=128,
-             dtype=attn.ATTN_DTYPE_BF16, scale=0.1, causal=1)
+             dtype=attn.ATTN_DTYPE_BF16, bt=None, maxp=0, page=0, scale=0.1, causal=1)
     a.update(kw)
     return attn.load().attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["S"],
-                                       a["mq"], a["mk"], a["H"], a["Hkv"], a["d"], a["dtype"], a["scale"],
-                                       a["causal"], None)
+                                       a["mq"], a["mk"], a["H"], a["Hkv"], a["d"], a["dtype"], a["bt"], a["maxp"],
+                                       a["page"], a["scale"], a["causal"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -97,6 +97,10 @@ def varlen(**kw):
     (dict(q=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
     (dict(Hkv=0), attn.ATTN_ERR_INVALID_ARG),
     (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(bt=FAKE, maxp=1, page=24), attn.ATTN_ERR_UNSUPPORTED),    # paged: power-of-two pages >= 16
+    (dict(bt=FAKE, maxp=4, page=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(bt=FAKE, maxp=0, page=16), attn.ATTN_ERR_INVALID_ARG),     # 0 pages < 16 keys
+    (dict(bt=FAKE, maxp=1, page=16, mk=17), attn.ATTN_ERR_INVALID_ARG),
     (dict(S=0), attn.ATTN_OK),
     (dict(mq=0), attn.ATTN_OK),
 ])

@@ -445,3 +445,71 @@ def test_store_kvcache_full_prefill(A):
     """The prefill store the bench times: 34069 tokens, 32 KV heads, d = 128, every slot."""
     w = synth.workload("store_prefill")
     _store_and_compare(A, w)
+
+
+# ------------------------------------------------------------------ paged prefill
+
+def _run_prefill(A, w):
+    import torch
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.cu_q), dev(w.cu_k), w.max_q,
+                               w.max_k, scale=w.scale, causal=w.causal, block_table=dev(w.block_table))
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("lq,lk,H,Hkv,d,page,causal", [
+    ([5, 130, 1, 64], [100, 130, 1000, 364], 8, 2, 128, 16, True),     # continued chunks
+    ([64, 65, 63], [64, 65, 63], 4, 4, 128, 16, True),                   # first chunks (no prefix)
+    ([200, 7], [777, 2000], 16, 8, 128, 32, True),
+    ([33, 1, 100], [33, 300, 101], 4, 1, 64, 64, True),
+    ([50, 129], [1000, 129], 8, 2, 64, 256, True),
+    ([40, 90], [300, 90], 4, 2, 128, 16, False),
+    ([0, 12, 3], [16, 12, 0], 4, 2, 128, 16, True),                      # empty query / empty context
+])
+def test_paged_prefill(A, lq, lk, H, Hkv, d, page, causal):
+    w = synth.paged_prefill(lq, lk, H, d, page, causal, seed=60, H_kv=Hkv)
+    o, lse = _run_prefill(A, w)
+    ro, rl = oracle.attention_varlen_paged(w.q, w.k_cache, w.v_cache, w.cu_q, w.cu_k, w.block_table, w.scale,
+                                           causal)
+    assert np.isfinite(o).all()   # no NaN-poisoned slot or padding page was read
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+def test_paged_prefill_equals_contiguous_varlen(A):
+    """Identity-ordered pages hold the same keys as a contiguous varlen batch."""
+    import torch
+    lens = [70, 300, 17]
+    w = synth.varlen(H=8, d=128, causal=True, seed=61, lens=lens, H_kv=2)
+    page = 16
+    n = [(L + page - 1) // page for L in lens]
+    kc = np.zeros((sum(n), page, 2, 128), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    bt = np.zeros((3, max(n)), dtype=np.int32)
+    off = 0
+    for s, L in enumerate(lens):
+        t = np.arange(L)
+        pages = off + t // page
+        kc[pages, t % page] = w.k[w.cu_k[s]:w.cu_k[s + 1]]
+        vc[pages, t % page] = w.v[w.cu_k[s]:w.cu_k[s + 1]]
+        bt[s, :n[s]] = np.arange(off, off + n[s])
+        off += n[s]
+    o1, l1 = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=True)
+    o2, l2 = A.attn_fwd_varlen(dev(w.q), dev(kc), dev(vc), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=True, block_table=dev(bt))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o1), host(o2)) and np.array_equal(host(l1), host(l2))
+
+
+def test_prefill_paged_full_sampled(A):
+    """The paged prefill the bench times: 16 sequences, the second half of each as new
+    causal query rows over its whole context in 16-token pages."""
+    w = synth.workload("prefill_paged")
+    o, lse = _run_prefill(A, w)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(103)
+    ro, rl = oracle.attention_varlen_paged(w.q, w.k_cache, w.v_cache, w.cu_q, w.cu_k, w.block_table, w.scale,
+                                           True, heads=[0, 19, 31], rows_per_seq=lambda s, L: _rows(L, rng, 8))
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
