@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # (KiB per dispatch), scaled by what the same counters read for a 512 MiB device copy
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
 # kernel source they were taken on (sha256 prefix); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "7ce42f6ccafc3fb0", "fetch_kib": 107071.0, "write_kib": 66560.0,
+FWD_COUNTERS = {"source_sha256_16": "561c4ed28083c2a8", "fetch_kib": 103176.0, "write_kib": 66588.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
