@@ -9,6 +9,8 @@ Contents
 ``attention``      the plain definition softmax(scale * Q K^T) V, two-pass, fp64
 ``online``         the tiled online-softmax recurrence, used only to pin ``attention``
 
+``backward``       gradients dQ, dK, dV of the same definition (chain rule, fp64)
+
 ``attention.store_kvcache`` is the plain scatter of new K/V rows into the page pools.
 
 Every function cites the passage of the source pages it follows.
@@ -26,4 +28,5 @@ from .attention import (  # noqa: F401
     probabilities,
     store_kvcache,
 )
+from .backward import attention_backward_dense, attention_backward_rows  # noqa: F401
 from .online import online_attention  # noqa: F401

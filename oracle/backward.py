@@ -1,0 +1,60 @@
+"""Gradients of exact attention in float64 (the oracle for the backward pass).
+TEST INFRASTRUCTURE.
+
+What is differentiated: O = softmax(scale * Q K^T) V row-wise, with the causal mask of
+the forward oracle (key j admissible for row i iff j <= i + (Lk - Lq)).  Given dO, the
+chain rule through the softmax gives, with P the probabilities:
+
+    dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij = dO_i . O_i,
+    dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+
+The pages describe the backward as recomputing S and P from the forward's stored
+statistics and dO, subtracting the row sums in dS, and keeping dQ in registers rather
+than adding it atomically (m.lqnn.cn FlashAttention article, section 4.3 and the
+pitfall list of section 6.4; "L2.5 SOTA Kernel", yulong.wang, section 2.3: P is
+recomputed from the O(N) logsumexp).  Here P is formed by the plain two-pass softmax,
+not from a stored statistic, so the oracle does not depend on the forward kernel.
+
+Grouped-query attention: the gradient of a KV head sums the contributions of every
+query head that reads it (query head h reads KV head h // (H / H_kv)).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _as_f64, kv_head, probabilities
+
+
+def attention_backward_rows(q, k, v, do, scale: float, causal: bool = False):
+    """One head: q [Lq, d], k [Lk, d], v [Lk, dv], do [Lq, dv] (floats or bf16 bits).
+    Returns (dq [Lq, d], dk [Lk, d], dv [Lk, dv]) in float64."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    lq, lk = q.shape[0], k.shape[0]
+    if lq == 0 or lk == 0:
+        return np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    p = probabilities(q, k, scale, causal)          # rows without keys are all zero
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = (p * dp).sum(axis=1, keepdims=True)      # D_i
+    ds = p * (dp - dsum)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward_dense(q, k, v, do, scale: float, causal: bool = False):
+    """Q, dO [B, H, N, d]; K, V [B, H_kv, Nk, d].  Returns dQ [B, H, N, d] and
+    dK, dV [B, H_kv, Nk, d] in float64 (KV-head gradients summed over their group)."""
+    B, H, N, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    dq = np.zeros((B, H, N, d))
+    dk = np.zeros((B, H_kv, Nk, d))
+    dv = np.zeros((B, H_kv, Nk, v.shape[3]))
+    for b in range(B):
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            a, bk, bv = attention_backward_rows(q[b, h], k[b, hk], v[b, hk], do[b, h], scale, causal)
+            dq[b, h] = a
+            dk[b, hk] += bk
+            dv[b, hk] += bv
+    return dq, dk, dv

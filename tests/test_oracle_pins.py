@@ -519,3 +519,65 @@ def test_paged_prefill_last_row_is_decode():
                                          bt, 0.5, True)
     od, ld = oracle.attention_decode_paged(q, kc, vc, bt, np.array(lk), 0.5)
     assert np.abs(o - od).max() < TIGHT and np.abs(l - ld).max() < TIGHT
+
+
+# ----------------------------------------------------------------- backward (gradients)
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = oracle.attention_rows(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("lq,lk,d,causal", [(3, 4, 2, False), (4, 4, 3, True), (2, 5, 2, True), (5, 3, 2, True)])
+def test_backward_matches_finite_differences(lq, lk, d, causal):
+    """Central differences of <O, dO> in float64 (independent of the chain rule)."""
+    r = rng(70 + lq * 10 + lk)
+    q, k, v, do = r.normal(size=(lq, d)), r.normal(size=(lk, d)), r.normal(size=(lk, d)), r.normal(size=(lq, d))
+    dq, dk, dv = oracle.attention_backward_rows(q, k, v, do, 0.7, causal)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            up = _loss(q, k, v, do, 0.7, causal)
+            x[idx] = x0 - eps
+            dn = _loss(q, k, v, do, 0.7, causal)
+            x[idx] = x0
+            assert abs((up - dn) / (2 * eps) - g[idx]) < 1e-7
+
+
+def test_backward_row_sum_identity():
+    """D_i = sum_j P_ij dP_ij equals dO_i . O_i: the row sum the backward subtracts."""
+    r = rng(75)
+    q, k, v, do = (r.normal(size=(6, 4)) for _ in range(4))
+    p = oracle.probabilities(q, k, 0.5, True)
+    o, _ = oracle.attention_rows(q, k, v, 0.5, True)
+    assert np.abs((p * (do @ v.T)).sum(axis=1) - (do * o).sum(axis=1)).max() < TIGHT
+
+
+def test_backward_gqa_sums_group_gradients():
+    """A KV head's gradient is the sum over the query heads reading it: equal to the
+    gradient of the explicitly expanded K/V summed back over the copies."""
+    r = rng(76)
+    q, do = r.normal(size=(1, 4, 5, 3)), r.normal(size=(1, 4, 5, 3))
+    k, v = r.normal(size=(1, 2, 6, 3)), r.normal(size=(1, 2, 6, 3))
+    dq, dk, dv = oracle.attention_backward_dense(q, k, v, do, 0.6, True)
+    dqe, dke, dve = oracle.attention_backward_dense(q, _expand_kv(k, 2, 1), _expand_kv(v, 2, 1), do, 0.6, True)
+    assert np.abs(dq - dqe).max() < TIGHT
+    assert np.abs(dk - dke.reshape(1, 2, 2, 6, 3).sum(axis=2)).max() < TIGHT
+    assert np.abs(dv - dve.reshape(1, 2, 2, 6, 3).sum(axis=2)).max() < TIGHT
+
+
+def test_backward_optional_autograd_crosscheck():
+    """torch autograd of the plain formula in float64 on the CPU (skipped without torch)."""
+    torch = pytest.importorskip("torch")
+    r = rng(77)
+    q, k, v, do = r.normal(size=(7, 4)), r.normal(size=(9, 4)), r.normal(size=(9, 4)), r.normal(size=(7, 4))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = (tq @ tk.T) * 0.5
+    mask = torch.arange(9)[None, :] <= torch.arange(7)[:, None] + 2
+    o = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=1) @ tv
+    o.backward(torch.tensor(do))
+    dq, dk, dv = oracle.attention_backward_rows(q, k, v, do, 0.5, True)
+    for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(a - b.numpy()).max() < 1e-12
