@@ -10,6 +10,7 @@ One step = one call of each entry point on its workload, inputs resident in HBM:
   attn_store_kvcache the varlen batch's 34069 new K/V rows written into 16-token pages
   attn_fwd_varlen    paged prefill: the second half of each of those sequences as new
                      causal rows over its whole context, read through the block table
+  attn_bwd           dQ, dK, dV of the dense causal forward (by recomputation)
 
 W untimed warm-up steps, then K timed steps; every kernel call is bracketed by HIP
 events on the stream it runs on.  Prints ONE JSON line.  `value` is the dense
@@ -112,7 +113,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache", "prefill_paged"],
+    ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache", "prefill_paged",
+                                       "bwd"],
                     default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -175,6 +177,11 @@ def main() -> int:
     w8.k_cache = w8.v_cache = None
     log(f"[bench] paged prefill workload ready ({time.perf_counter() - t:.1f} s)")
 
+    do3 = dev(synth.normal(0, synth.T_DO, (1, 32, 8192, 128), True))
+    dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+    wsb = torch.empty(attn.attn_bwd_workspace_size(1, 32, 8192), dtype=torch.uint8, device="cuda")
+    log(f"[bench] backward workload ready ({time.perf_counter() - t:.1f} s)")
+
     w7 = synth.workload("store_prefill")
     k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
     sl7 = torch.from_numpy(w7.slot_mapping).cuda()
@@ -195,12 +202,15 @@ def main() -> int:
     def run_store():
         attn.attn_store_kvcache(k7, v7, kc7, vc7, sl7)
 
+    def run_bwd():
+        attn.attn_bwd(q3, k3, v3, o3, l3, do3, scale=w3.scale, causal=True, dq=dq3, dk=dk3, dv=dv3, workspace=wsb)
+
     def run_prefill_paged():
         attn.attn_fwd_varlen(q8, kc8, vc8, cq8, ck8, w8.max_q, w8.max_k, scale=w8.scale, causal=True,
                              out=o8, lse=l8, block_table=bt8)
 
     parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa),
-             ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged)]
+             ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged), ("bwd", run_bwd)]
     if args.only:
         parts = [p for p in parts if p[0] == args.only]
 
@@ -266,6 +276,13 @@ def main() -> int:
                              "ms": ms["decode_gqa"].mean(), "GB/s": by6 / t6 / 1e9, "peak": PEAK_HBM_GBS,
                              "frac": by6 / t6 / 1e9 / PEAK_HBM_GBS, "bytes_per_launch": by6,
                              "note": "KV bytes counted once per KV head (grouped-query)"}
+    if "bwd" in ms:
+        tb = ms["bwd"].mean() / 1e3
+        flb = 2.5 * fl3   # five tile products per admissible pair (dV, dP, dQ, dK, and S)
+        res["bwd"] = {"workload": "backward of the causal B=1 H=32 N=8192 d=128 forward (dQ, dK, dV)",
+                      "ms": ms["bwd"].mean(), "tflops": flb / tb / 1e12, "frac": flb / tb / 1e12 / PEAK_BF16_TFLOPS,
+                      "flops_per_launch": flb,
+                      "note": "algorithmic flops 2.5x the forward's; the kernels recompute S and P twice"}
     if "prefill_paged" in ms:
         t8 = ms["prefill_paged"].mean() / 1e3
         lq8, lk8 = w8.lens_q.astype(np.float64), w8.lens_k.astype(np.float64)

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     AttnError,
+    attn_bwd,
+    attn_bwd_workspace_size,
     attn_decode_paged,
     attn_decode_paged_workspace_size,
     attn_fwd,

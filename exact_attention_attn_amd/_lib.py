@@ -18,7 +18,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
-           "attn_store_kvcache", "attn_status_string", "attn_version")
+           "attn_store_kvcache", "attn_bwd", "attn_bwd_workspace_size", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -50,6 +50,10 @@ def load() -> ctypes.CDLL:
     i64 = ctypes.c_int64
     lib.attn_store_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
     lib.attn_store_kvcache.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.attn_bwd.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -229,3 +233,38 @@ def attn_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None):
                                 k.stride(0), v.stride(0), num_pages, page, _dtype_code(k), _stream(stream))
     _check(rc, "attn_store_kvcache")
     return k_cache, v_cache
+
+
+def attn_bwd_workspace_size(B: int, H: int, N: int) -> int:
+    return int(load().attn_bwd_workspace_size(B, H, N))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Gradients of attn_fwd.  q, o, dout [B, H, N, d]; k, v [B, H_kv, Nk, d] (contiguous
+    bf16); lse float32 [B, H, N] from the forward.  Returns (dq, dk, dv)."""
+    torch = _torch()
+    lib = load()
+    B, H, N, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("o and dout must match q, lse must be [B, H, N]")
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("backward tensors must be contiguous")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_size(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+    rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Hkv, N, Nk, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv

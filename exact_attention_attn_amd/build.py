@@ -15,8 +15,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_kvcache.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_kvcache.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
+
+# Per-source extra flags.  The backward keeps its dK / dV accumulators in AGPRs through
+# inline asm and the other MFMA results in VGPRs (-amdgpu-mfma-vgpr-form), where VALU
+# reads them.
+EXTRA_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU ops are kept out of the generated code (-packed-fp32-ops).
 HIPFLAGS = [
@@ -34,7 +39,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

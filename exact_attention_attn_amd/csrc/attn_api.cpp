@@ -204,6 +204,45 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
   return check_launch(attn::launch_decode_paged(p, d, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_workspace_size(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)B * H * N * 2 * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int Nk, int d, int dtype,
+             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || Nk < 0) return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)B * H == 0 || (int64_t)N + Nk == 0) return ATTN_OK;  // no gradient entries
+  const bool rows = N > 0, keys = Nk > 0;
+  if (rows && (!q || !o || !dout || !lse || !dq)) return fail(ATTN_ERR_INVALID_ARG);
+  if (keys && (!k || !v || !dk || !dv)) return fail(ATTN_ERR_INVALID_ARG);
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  const size_t need = attn_bwd_workspace_size(B, H, N);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u)))
+    return fail(ATTN_ERR_INVALID_ARG);
+  // 32-bit byte offsets of one 32-row tile
+  if ((int64_t)32 * d * 2 > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED);
+
+  attn::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.ws = static_cast<float*>(workspace);
+  p.B = B; p.H = H; p.H_kv = H_kv; p.N = N; p.Nk = Nk;
+  p.kv_group = H / H_kv;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  return check_launch(attn::launch_bwd(p, d, causal != 0, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
                        const int64_t* slot_mapping, int T, int H_kv, int d,
                        int64_t k_token_stride, int64_t v_token_stride,

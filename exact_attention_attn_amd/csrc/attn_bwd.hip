@@ -1,0 +1,404 @@
+// Backward pass of exact attention for gfx950: dQ, dK, dV by recomputation.
+//
+// Method: the forward keeps only O and the per-row logsumexp; the backward recomputes
+// S and P from them, takes dO, and applies the chain rule through the softmax
+// (m.lqnn.cn FlashAttention article, section 4.3: recompute P, use dO, subtract the row
+// sums in dS; "L2.5 SOTA Kernel", yulong.wang, section 2.3: P from the stored
+// logsumexp).  With D_i = dO_i . O_i:
+//     P = exp(scale q k^T - lse),  dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),
+//     dQ = scale dS K,             dK = scale dS^T Q.
+// No float atomics (the same article's advice against atomically accumulating dQ):
+//  * bwd_delta_kernel writes (lse log2 e, D) per query row into the workspace;
+//  * bwd_dq_kernel owns query rows (4 wavefronts x 32 rows) and streams key tiles of 32,
+//    holding dQ in registers: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
+//  * bwd_dkdv_kernel owns keys (4 wavefronts x 32 keys) and streams query tiles of 32
+//    of every query head that reads its KV head, holding dK and dV in registers:
+//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
+// Both recompute S and P (seven tile products per pair of tiles instead of five) so
+// that every gradient is written exactly once.
+//
+// MFMA mapping (v_mfma_f32_32x32x16_bf16): as in the forward kernel, a 32x32 accumulator
+// gives each lane one column (a query in the dQ kernel, a key in the dK/dV kernel) and
+// 16 rows; the bf16 P or dS feeds the next product as the B operand straight from the
+// accumulator, and the A operand of that product (K^T, dO^T, Q^T) is read from LDS with
+// transposing reads in the accumulator's row order.  Tiles go global -> LDS with
+// direct-to-LDS loads, each tensor in the layout its product needs ("operand order" for
+// A operands read 16 bytes per lane, "transposed" for the ds_read_b64_tr_b16 operands).
+#include "attn_internal.h"
+#include "attn_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634074f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+// Byte offsets of one wavefront's 1 KiB direct-to-LDS blocks of a [R rows, D] tile
+// (R = 32): "operand order" (block (t): rows lane % 32, 16-byte chunk 2t + lane / 32) and
+// "transposed" (block (db, r16): rows 16 r16 + lane / 4, chunk 4 db + lane % 4).
+template <int D, int BPW>
+struct TileOffsets {
+  int orow[BPW], ocol[BPW], trow[BPW], tcol[BPW];
+  __device__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = wave * BPW + i;
+      orow[i] = lane & 31;
+      ocol[i] = (2 * bi + (lane >> 5)) * 16;
+      trow[i] = 16 * (bi & 1) + lane / 4;
+      tcol[i] = (32 * (bi >> 1) + 8 * (lane % 4)) * 2;
+    }
+  }
+};
+
+// Load rows [r0, r0 + 32) of a row-major tensor (row stride `rs` elements) into an LDS
+// tile in operand order (TR = false) or transposed order (TR = true); rows at or past
+// `nrows` are clamped to the last row (they are masked by the caller).
+template <int D, int BPW, bool TR>
+__device__ __forceinline__ void load_tile(const uint16_t* base, int64_t rs, int r0, int nrows, uint8_t* lds,
+                                          const TileOffsets<D, BPW>& to, int wave) {
+  const int last = nrows - r0 - 1;  // >= 0
+  const u32x4s r = buffer_rsrc(base + (int64_t)r0 * rs, ((int64_t)last * rs + D) * 2);
+  const int rbytes = (int)rs * 2;
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int row = min(TR ? to.trow[i] : to.orow[i], last);
+    dma16(r, lds + (wave * BPW + i) * 1024, row * rbytes + (TR ? to.tcol[i] : to.ocol[i]));
+  }
+}
+
+// A operand of k-step t from an operand-order tile (16 bytes per lane)
+__device__ __forceinline__ bf16x8 op_read(const uint8_t* tile, int lane, int t) {
+  return as_bf16x8(*(const lds_u32x4*)(tile + lane * 16 + t * 1024));
+}
+// Transposed A operand (columns 32 db .. 32 db + 31, rows in accumulator order for the
+// 16-row group t4) from a transposed tile: two ds_read_b64_tr_b16
+__device__ __forceinline__ bf16x8 tr_read(const uint8_t* tile, int lane, int db, int t4) {
+  const int half = lane >> 5;
+  const int off = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  const uint8_t* p = tile + off + db * 2048 + t4 * 1024;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 512));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Accumulator element v of lane (half = lane / 32) sits in row 8 (v / 4) + 4 half + v % 4.
+__device__ __forceinline__ int acc_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
+
+// 32x32 accumulator -> 16 rows of one column, written as bf16 rows of a row-major
+// tensor: lane's column is the output row, accumulator rows are output columns.
+template <int DB>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, float mul, int half) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 r0 = (__bf16)(acc[db][4 * i + 0] * mul), r1 = (__bf16)(acc[db][4 * i + 1] * mul);
+      const __bf16 r2 = (__bf16)(acc[db][4 * i + 2] * mul), r3 = (__bf16)(acc[db][4 * i + 3] * mul);
+      const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
+      const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
+      *(u32x2*)(dst + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
+    }
+}
+
+// acc += A B on an AGPR-pinned accumulator (the dK / dV accumulators: the dK/dV kernel
+// needs more than 256 registers).  The hazard recognizer does not see inside inline
+// asm, so the callers spell out the wait states: after VALU writes of an operand before
+// the first of these MFMAs, and after the last of them before a VALU read of the
+// accumulator (agpr_settle).  MFMAs chained on the same accumulator need none.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// ------------------------------------------------------------------------------------
+// (lse log2 e, D = dO . O) per query row
+// ------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;        // rows per workgroup
+  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)((const uint16_t*)p.dout + row * D + 8 * c);
+    const u32x4 b = *(const u32x4*)((const uint16_t*)p.o + row * D + 8 * c);
+    const unsigned av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = __builtin_fmaf(__builtin_bit_cast(float, av[i] << 16), __builtin_bit_cast(float, bv[i] << 16), s);
+      s = __builtin_fmaf(__builtin_bit_cast(float, av[i] & 0xFFFF0000u), __builtin_bit_cast(float, bv[i] & 0xFFFF0000u), s);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
+  if (row < rows && c == 0) *(float2*)(p.ws + 2 * row) = make_float2(p.lse[row] * kLog2e, s);
+}
+
+// ------------------------------------------------------------------------------------
+// dQ: 4 wavefronts x 32 query rows of one (b, h); key tiles of 32
+// ------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(const BwdParams p) {
+  constexpr int NW = 4, BM = 32 * NW, BN = 32;
+  constexpr int DT = D / 16, DB = D / 32;
+  constexpr int TILE = BN * D * 2;          // bytes of one [32, D] bf16 tile
+  constexpr int BPW = TILE / 1024 / NW;     // 1 KiB blocks per wavefront per tile
+  static_assert(BPW * NW * 1024 == TILE, "tile split");
+  // per buffer: K (operand order), K (transposed), V (operand order)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 3 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int npairs = p.B * p.H;
+  const int pair = blockIdx.x % npairs, rbi = blockIdx.x / npairs;
+  const int n_rb = (p.N + BM - 1) / BM;
+  const int rb = CAUSAL ? n_rb - 1 - rbi : rbi;  // heaviest row block first
+  const int b = pair / p.H, h = pair - b * p.H, hk = h / p.kv_group;
+  const int Lq = p.N, Lk = p.Nk, shift = Lk - Lq;
+  const int row0 = rb * BM;
+  const int qi = row0 + wave * 32 + (lane & 31);
+  const uint16_t* Q = (const uint16_t*)p.q + ((int64_t)b * p.H + h) * Lq * D;
+  const uint16_t* dO = (const uint16_t*)p.dout + ((int64_t)b * p.H + h) * Lq * D;
+  const uint16_t* K = (const uint16_t*)p.k + ((int64_t)b * p.H_kv + hk) * Lk * D;
+  const uint16_t* V = (const uint16_t*)p.v + ((int64_t)b * p.H_kv + hk) * Lk * D;
+
+  int kend = Lk;
+  if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
+  const int ntiles = (kend + BN - 1) / BN;
+  int nfull = Lk / BN;  // tiles that need no mask for any row of this workgroup
+  if (CAUSAL) nfull = min(nfull, max(0, (row0 + shift + 1) / BN));
+
+  bf16x8 qreg[DT], dreg[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (qi < Lq) {
+      a = *(const u32x4*)(Q + (int64_t)qi * D + 16 * t + 8 * half);
+      c = *(const u32x4*)(dO + (int64_t)qi * D + 16 * t + 8 * half);
+    }
+    qreg[t] = as_bf16x8(a);
+    dreg[t] = as_bf16x8(c);
+  }
+  float lse2 = 0.f, dsum = 0.f;
+  if (qi < Lq) {
+    const float2 ld = *(const float2*)(p.ws + 2 * (((int64_t)b * p.H + h) * Lq + qi));
+    lse2 = ld.x;
+    dsum = ld.y;
+  }
+  const float c2 = p.scale_log2;
+
+  TileOffsets<D, BPW> to;
+  to.init(wave, lane);
+  auto issue = [&](int j) {
+    uint8_t* buf = smem + (j & 1) * 3 * TILE;
+    load_tile<D, BPW, false>(K, D, j * BN, Lk, buf, to, wave);
+    load_tile<D, BPW, true>(K, D, j * BN, Lk, buf + TILE, to, wave);
+    load_tile<D, BPW, false>(V, D, j * BN, Lk, buf + 2 * TILE, to, wave);
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  if (ntiles > 0) issue(0);
+  for (int j = 0; j < ntiles; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's share of tile j landed
+    __syncthreads();                                   // ... every wave's; tile j-1 is free
+    if (j + 1 < ntiles) issue(j + 1);
+    const uint8_t* buf = smem + (j & 1) * 3 * TILE;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf, lane, t), qreg[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf + 2 * TILE, lane, t), dreg[t], dp, 0, 0, 0);
+    }
+    // dS^T = P^T (dP^T - D); keys past the end or above the diagonal have P = 0
+    const int base = j * BN + 4 * half;
+    int lim = BN;  // element offsets <= lim are admissible
+    if (j >= nfull) {
+      lim = Lk - 1 - base;
+      if (CAUSAL) lim = min(lim, qi + shift - base);
+    }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int off = 8 * (v >> 2) + (v & 3);
+      const float pv = off <= lim ? exp2_fast(__builtin_fmaf(s[v], c2, -lse2)) : 0.f;
+      dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dsum));
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(buf + TILE, lane, db, t4), dsb[t4], acc[db], 0, 0, 0);
+  }
+  if (qi < Lq) store_rows<DB>((uint16_t*)p.dq + ((int64_t)b * p.H + h) * Lq * D + (int64_t)qi * D, acc, p.scale, half);
+}
+
+// ------------------------------------------------------------------------------------
+// dK, dV: 4 wavefronts x 32 keys of one (b, KV head); query tiles of 32 of every query
+// head of the group
+// ------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NW = 4, BK = 32 * NW, BQ = 32;
+  constexpr int DT = D / 16, DB = D / 32;
+  constexpr int TILE = BQ * D * 2;
+  constexpr int BPW = TILE / 1024 / NW;
+  static_assert(BPW * NW * 1024 == TILE, "tile split");
+  // per buffer: Q (operand order), Q (transposed), dO (operand order), dO (transposed),
+  // then the tile's 32 (lse log2 e, D) pairs
+  constexpr int BUF = 4 * TILE + 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int npairs = p.B * p.H_kv;
+  const int pair = blockIdx.x % npairs, kb = blockIdx.x / npairs;  // low (heaviest) key blocks first
+  const int b = pair / p.H_kv, hk = pair - b * p.H_kv;
+  const int Lq = p.N, Lk = p.Nk, shift = Lk - Lq;
+  const int k0 = kb * BK;
+  const int key = k0 + wave * 32 + (lane & 31);  // this lane's key (accumulator column)
+  const int G = p.kv_group;
+  const uint16_t* K = (const uint16_t*)p.k + ((int64_t)b * p.H_kv + hk) * Lk * D;
+  const uint16_t* V = (const uint16_t*)p.v + ((int64_t)b * p.H_kv + hk) * Lk * D;
+
+  bf16x8 kreg[DT], vreg[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (key < Lk) {
+      a = *(const u32x4*)(K + (int64_t)key * D + 16 * t + 8 * half);
+      c = *(const u32x4*)(V + (int64_t)key * D + 16 * t + 8 * half);
+    }
+    kreg[t] = as_bf16x8(a);
+    vreg[t] = as_bf16x8(c);
+  }
+  const float c2 = p.scale_log2;
+
+  // query tiles of one head that can see any key of this block
+  const int qfirst = CAUSAL ? max(0, k0 - shift) / BQ : 0;
+  const int nqt = (Lq + BQ - 1) / BQ;
+  const int per_head = max(0, nqt - qfirst);
+  const int nsteps = G * per_head;
+
+  TileOffsets<D, BPW> to;
+  to.init(wave, lane);
+  auto issue = [&](int st) {
+    const int h = hk * G + st / per_head;
+    const int qt0 = (qfirst + st % per_head) * BQ;
+    const uint16_t* Q = (const uint16_t*)p.q + ((int64_t)b * p.H + h) * Lq * D;
+    const uint16_t* dO = (const uint16_t*)p.dout + ((int64_t)b * p.H + h) * Lq * D;
+    uint8_t* buf = smem + (st & 1) * BUF;
+    load_tile<D, BPW, false>(Q, D, qt0, Lq, buf, to, wave);
+    load_tile<D, BPW, true>(Q, D, qt0, Lq, buf + TILE, to, wave);
+    load_tile<D, BPW, false>(dO, D, qt0, Lq, buf + 2 * TILE, to, wave);
+    load_tile<D, BPW, true>(dO, D, qt0, Lq, buf + 3 * TILE, to, wave);
+    if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i
+      const int last = Lq - qt0 - 1;
+      const float* ws = p.ws + 2 * (((int64_t)b * p.H + h) * Lq + qt0);
+      const u32x4s r = buffer_rsrc(ws, ((int64_t)last + 1) * 8);
+      const int voff = min(lane >> 1, last) * 8 + (lane & 1) * 4;
+      const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)(buf + 4 * TILE));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0v), "v"(voff), "s"(r)
+                   : "memory", "m0");
+    }
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  if (nsteps > 0) issue(0);
+  for (int st = 0; st < nsteps; ++st) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (st + 1 < nsteps) issue(st + 1);
+    const uint8_t* buf = smem + (st & 1) * BUF;
+    const int qt0 = (qfirst + st % per_head) * BQ;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf, lane, t), kreg[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf + 2 * TILE, lane, t), vreg[t], dp, 0, 0, 0);
+    }
+    // P and dS for the 16 query rows of this lane's accumulator column (its key)
+    const float* ld = (const float*)(buf + 4 * TILE);
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 8 * g4 + 4 * half;  // 4 consecutive query rows
+      const f32x4 a = *(const lds_f32x4*)(ld + 2 * r0);
+      const f32x4 c = *(const lds_f32x4*)(ld + 2 * r0 + 4);
+      const float l2[4] = {a.x, a.z, c.x, c.z}, dd[4] = {a.y, a.w, c.y, c.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * g4 + e;
+        const int q = qt0 + r0 + e;
+        const bool ok = q < Lq && key < Lk && (!CAUSAL || key <= q + shift);
+        const float pv = ok ? exp2_fast(__builtin_fmaf(s[v], c2, -l2[e])) : 0.f;
+        pb[v >> 3][v & 7] = (__bf16)pv;
+        dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dd[e]));
+      }
+    }
+    // The asm MFMAs below read P and dS, just written by VALU: the hazard recognizer does
+    // not see them, so five wait states are spelled out here, after the last write (the
+    // operands are tied to this statement so that no write can move past it).
+    asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]), "+v"(dsb[0]), "+v"(dsb[1]));
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4) {
+        mfma_agpr(dv[db], tr_read(buf + 3 * TILE, lane, db, t4), pb[t4]);
+        mfma_agpr(dk[db], tr_read(buf + TILE, lane, db, t4), dsb[t4]);
+      }
+  }
+  agpr_settle();
+  if (key < Lk) {
+    const int64_t row = ((int64_t)b * p.H_kv + hk) * Lk * D + (int64_t)key * D;
+    store_rows<DB>((uint16_t*)p.dk + row, dk, p.scale, half);
+    store_rows<DB>((uint16_t*)p.dv + row, dv, 1.0f, half);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  if (rows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nq = (int64_t)((p.N + 127) / 128) * p.B * p.H;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nq), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nk = (int64_t)((p.Nk + 127) / 128) * p.B * p.H_kv;
+  if (nk > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nk), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 128) return causal ? launch_bwd_t<128, true>(p, s) : launch_bwd_t<128, false>(p, s);
+  return causal ? launch_bwd_t<64, true>(p, s) : launch_bwd_t<64, false>(p, s);
+}
+
+}  // namespace attn

@@ -72,11 +72,30 @@ struct StoreParams {
   int row_bytes;            // H_kv * d * element size
 };
 
+// Parameters of one backward launch (contiguous bf16 tensors).
+struct BwdParams {
+  const void* q;      // [B, H, N, d]
+  const void* k;      // [B, H_kv, Nk, d]
+  const void* v;
+  const void* o;      // [B, H, N, d]
+  const void* dout;   // [B, H, N, d]
+  const float* lse;   // [B, H, N] (natural log)
+  void* dq;           // [B, H, N, d]
+  void* dk;           // [B, H_kv, Nk, d]
+  void* dv;
+  float* ws;          // [B, H, N, 2]: (lse * log2 e, dO . O) per query row
+  int B, H, H_kv, N, Nk;
+  int kv_group;       // H / H_kv
+  float scale;
+  float scale_log2;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);  // paged iff p.block_table
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_store_kvcache(const StoreParams& p, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 // Wavefronts per workgroup of the bf16 forward kernel; each owns 32 query rows.
 #ifndef ATTN_FWD_NW

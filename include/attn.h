@@ -13,7 +13,8 @@
  *                       K/V, read page by page through a block table
  *                       (sections 3.4 and "PagedAttention");
  *   attn_store_kvcache  the step's new K/V rows written into the page pools
- *                       through slot_mapping.
+ *                       through slot_mapping;
+ *   attn_bwd            the gradients dQ, dK, dV of attn_fwd by recomputation.
  *
  * Each computes, per query row i, O_i = sum_j softmax_j(scale * q_i . k_j) v_j over
  * the admissible keys j, and the row's logsumexp lse_i = ln sum_j exp(scale * q_i . k_j)
@@ -168,6 +169,33 @@ int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cach
                        const int64_t* slot_mapping, int T, int H_kv, int d,
                        int64_t k_token_stride, int64_t v_token_stride,
                        int num_pages, int page_size, int dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_size — bytes of device workspace attn_bwd needs (0 if none).
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N);
+
+/*
+ * attn_bwd — gradients of dense attention by recomputation (bfloat16).
+ *
+ * The forward keeps only O and lse; the backward recomputes S and P from them and dO
+ * and applies the chain rule through the softmax (m.lqnn.cn FlashAttention article,
+ * section 4.3; yulong.wang "L2.5 SOTA Kernel", section 2.3).  With D_i = dO_i . O_i:
+ * dV = P^T dO, dS = P (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q; the gradient of
+ * a KV head sums over the query heads that read it (grouped-query attention).
+ *
+ * q, o, dout, dq : [B, H, N, d] contiguous;  k, v, dk, dv : [B, H_kv, Nk, d] contiguous;
+ * lse : float32 [B, H, N], the forward's logsumexp (natural log) for the same q, k, v,
+ *       scale and causal flag (attn_fwd's lse output).
+ * dq, dk, dv are overwritten (not accumulated into).  Every gradient entry is written
+ * exactly once, without atomics, so the result is deterministic.
+ * workspace : at least attn_bwd_workspace_size(B, H, N) bytes, 8-byte aligned, owned by
+ *       the caller; its contents on entry do not matter.
+ * dtype : ATTN_DTYPE_BF16 only; d 64 or 128; causal bottom-right as in attn_fwd.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int Nk, int d, int dtype,
+             float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

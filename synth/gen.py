@@ -30,7 +30,7 @@ CHUNK = 1 << 22
 BF16_NAN = np.uint16(0x7FC0)
 
 # tensor ids (part of the recipe: changing one changes every drawn value)
-T_Q, T_K, T_V, T_KCACHE, T_VCACHE = 1, 2, 3, 4, 5
+T_Q, T_K, T_V, T_KCACHE, T_VCACHE, T_DO = 1, 2, 3, 4, 5, 6
 
 
 def _threads() -> int:

@@ -178,3 +178,37 @@ def store(**kw):
 ])
 def test_store_kvcache_rejects_before_launch(kw, status):
     assert store(**kw) == status
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=4, Hkv=2, N=64,
+             Nk=64, d=128, dtype=attn.ATTN_DTYPE_BF16, scale=0.1, causal=1, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return attn.load().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["B"], a["H"], a["Hkv"], a["N"], a["Nk"], a["d"], a["dtype"], a["scale"],
+                                a["causal"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dk=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(do=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(wsb=64 * 4 * 8 - 1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dq=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(B=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), attn.ATTN_OK),
+    (dict(N=0, Nk=0), attn.ATTN_OK),
+])
+def test_bwd_rejects_before_launch(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    assert attn.attn_bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 8
+    assert attn.attn_bwd_workspace_size(0, 3, 5) == 0

@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from tests.golden.load import load
-from tests.util import TOL_BF16_LSE, TOL_BF16_O, TOL_F32, assert_close, dev, host
+from tests.util import TOL_BF16_LSE, TOL_BF16_O, TOL_F32, assert_close, dev, host, max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -513,3 +513,69 @@ def test_prefill_paged_full_sampled(A):
                                            True, heads=[0, 19, 31], rows_per_seq=lambda s, L: _rows(L, rng, 8))
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
+# ------------------------------------------------------------------ backward
+
+TOL_BWD_REL = 2e-2   # max-abs error over max |reference| per gradient tensor
+
+
+def _bwd_case(A, B, H, Hkv, N, Nk, d, causal, seed):
+    import torch
+    w = synth.dense(B, H, N, d, "bf16", causal, seed=seed, Nk=Nk, H_kv=Hkv)
+    do = synth.normal(seed, synth.T_DO, (B, H, N, d), True)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=causal)
+    dq, dk, dv = A.attn_bwd(q, k, v, o, lse, dev(do), scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    return w, do, host(dq), host(dk), host(dv)
+
+
+def _assert_grad(name, got, want):
+    scale = max(1e-30, float(np.abs(want).max()))
+    err, where, _ = max_err(got, want)
+    print(f"  {name}: max|err| = {err:.3e} at {where}, max|ref| = {scale:.3e}, rel {err / scale:.2e}", flush=True)
+    assert np.isfinite(got).all(), f"{name}: non-finite entries"
+    assert err <= TOL_BWD_REL * scale, f"{name}: max|err| {err:.3e} > {TOL_BWD_REL} x {scale:.3e}"
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,Nk,d,causal", [
+    (2, 4, 4, 256, 256, 128, True),
+    (1, 8, 2, 300, 300, 64, True),      # grouped-query, ragged tiles
+    (1, 4, 4, 200, 333, 128, False),     # Nk != N
+    (1, 2, 1, 333, 200, 128, True),      # rows without keys (bottom-right), multi-query
+    (2, 2, 2, 64, 64, 64, False),
+    (1, 2, 2, 1, 77, 128, True),         # one query row
+])
+def test_backward(A, B, H, Hkv, N, Nk, d, causal):
+    w, do, dq, dk, dv = _bwd_case(A, B, H, Hkv, N, Nk, d, causal, seed=80)
+    rq, rk, rv = oracle.attention_backward_dense(w.q, w.k, w.v, do, w.scale, causal)
+    _assert_grad("dQ", dq, rq)
+    _assert_grad("dK", dk, rk)
+    _assert_grad("dV", dv, rv)
+
+
+def test_backward_deterministic(A):
+    a = _bwd_case(A, 1, 4, 2, 257, 257, 128, True, seed=81)
+    b = _bwd_case(A, 1, 4, 2, 257, 257, 128, True, seed=81)
+    for x, y in zip(a[2:], b[2:]):
+        assert np.array_equal(x, y)
+
+
+def test_backward_full_causal_8192(A):
+    """The backward the bench times: causal B=1 H=32 N=8192 d=128, two heads checked
+    in full against the oracle."""
+    import torch
+    w = synth.workload("c3")
+    do = synth.normal(0, synth.T_DO, (1, 32, 8192, 128), True)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=True)
+    dq, dk, dv = A.attn_bwd(q, k, v, o, lse, dev(do), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    dq, dk, dv = host(dq), host(dk), host(dv)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    for h in (0, 31):
+        rq, rk, rv = oracle.attention_backward_rows(w.q[0, h], w.k[0, h], w.v[0, h], do[0, h], w.scale, True)
+        _assert_grad(f"dQ[h={h}]", dq[0, h], rq)
+        _assert_grad(f"dK[h={h}]", dk[0, h], rk)
+        _assert_grad(f"dV[h={h}]", dv[0, h], rv)
