@@ -41,8 +41,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # HBM bytes per launch of the dense forward kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch), scaled by what the same counters read for a 512 MiB device copy
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
-# kernel source they were taken on (sha256 prefix); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "561c4ed28083c2a8", "fetch_kib": 103176.0, "write_kib": 66588.0,
+# kernel source they were taken on (sha256 prefix of attn_fwd.hip followed by the
+# attn_tile.h it includes); reported as null otherwise.
+FWD_COUNTERS = {"source_sha256_16": "40f80cd71fcea801", "fetch_kib": 103932.0, "write_kib": 66577.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -76,9 +77,11 @@ def fwd_traffic_bytes():
     """Counter-measured HBM bytes per dense forward launch, or None if the kernel source
     changed since the counters were taken."""
     import hashlib
-    src = os.path.join(ROOT, "exact_attention_attn_amd", "csrc", "attn_fwd.hip")
-    with open(src, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("attn_fwd.hip", "attn_tile.h"):
+        with open(os.path.join(ROOT, "exact_attention_attn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    h = h.hexdigest()[:16]
     c = FWD_COUNTERS
     if h != c["source_sha256_16"]:
         return None
