@@ -113,6 +113,34 @@ __device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void agpr_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// Registers loaded from global memory before the tile loop are passed through an empty
+// asm statement, so the compiler waits for those loads here, once.  Otherwise its wait
+// for them lands inside the loop as a vmcnt(0), which would also wait for every
+// direct-to-LDS prefetch in flight.
+template <int N>
+__device__ __forceinline__ void settle(bf16x8 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// Tiles stream through a ring of STAGES LDS buffers, STAGES - 1 ahead of use.  Before
+// using a stage, a wavefront waits for its own L direct-to-LDS loads of that stage while
+// up to `later` (<= STAGES - 2) younger stages stay in flight: loads complete in issue
+// order, so vmcnt(later * L) suffices (a wavefront that issued more than L loads for a
+// stage waits a little longer than needed).
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+template <int L, int STAGES>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (STAGES >= 4) {
+    if (later >= 2) { wait_vm<2 * L>(); return; }
+  }
+  if constexpr (STAGES >= 3) {
+    if (later >= 1) { wait_vm<L>(); return; }
+  }
+  wait_vm<0>();
+}
+
 // ------------------------------------------------------------------------------------
 // (lse log2 e, D = dO . O) per query row
 // ------------------------------------------------------------------------------------
@@ -149,8 +177,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int TILE = BN * D * 2;          // bytes of one [32, D] bf16 tile
   constexpr int BPW = TILE / 1024 / NW;     // 1 KiB blocks per wavefront per tile
   static_assert(BPW * NW * 1024 == TILE, "tile split");
-  // per buffer: K (operand order), K (transposed), V (operand order)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 3 * TILE];
+#ifndef BWD_DQ_STAGES
+#define BWD_DQ_STAGES 2
+#endif
+  constexpr int STAGES = BWD_DQ_STAGES;
+  // per stage: K (operand order), K (transposed), V (operand order)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 3 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,12 +222,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     lse2 = ld.x;
     dsum = ld.y;
   }
+  settle(qreg);
+  settle(dreg);
+  asm volatile("" : "+v"(lse2), "+v"(dsum));
   const float c2 = p.scale_log2;
 
   TileOffsets<D, BPW> to;
   to.init(wave, lane);
   auto issue = [&](int j) {
-    uint8_t* buf = smem + (j & 1) * 3 * TILE;
+    uint8_t* buf = smem + (j % STAGES) * 3 * TILE;
     load_tile<D, BPW, false>(K, D, j * BN, Lk, buf, to, wave);
     load_tile<D, BPW, true>(K, D, j * BN, Lk, buf + TILE, to, wave);
     load_tile<D, BPW, false>(V, D, j * BN, Lk, buf + 2 * TILE, to, wave);
@@ -205,18 +240,43 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  if (ntiles > 0) issue(0);
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (j < ntiles) issue(j);
   for (int j = 0; j < ntiles; ++j) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's share of tile j landed
-    __syncthreads();                                   // ... every wave's; tile j-1 is free
-    if (j + 1 < ntiles) issue(j + 1);
-    const uint8_t* buf = smem + (j & 1) * 3 * TILE;
+    wait_stage<3 * BPW, STAGES>(min(STAGES - 2, ntiles - 1 - j));  // this wave's share of tile j
+    __syncthreads();  // ... and every wave's; the stage of tile j-1 is free
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
+    const uint8_t* buf = smem + (j % STAGES) * 3 * TILE;
+    // S^T = K Q^T and dP^T = V dO^T, operands read KPF k-steps ahead of their products
+    constexpr int KPF = 3;
+    bf16x8 ka[KPF], va[KPF];
+#pragma unroll
+    for (int u = 0; u < KPF; ++u) {
+      ka[u] = op_read(buf, lane, u);
+      va[u] = op_read(buf + 2 * TILE, lane, u);
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf, lane, t), qreg[t], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf + 2 * TILE, lane, t), dreg[t], dp, 0, 0, 0);
+      bf16x8 kn = ka[t % KPF], vn = va[t % KPF];
+      if (t + KPF < DT) {
+        kn = op_read(buf, lane, t + KPF);
+        vn = op_read(buf + 2 * TILE, lane, t + KPF);
+      }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % KPF], qreg[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % KPF], dreg[t], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      ka[t % KPF] = kn;
+      va[t % KPF] = vn;
     }
+    // the dQ product's operands are requested while S and dP are computed
+    bf16x8 kt[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = tr_read(buf + TILE, lane, db, t4);
+    __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); keys past the end or above the diagonal have P = 0
     const int base = j * BN + 4 * half;
     int lim = BN;  // element offsets <= lim are admissible
@@ -236,7 +296,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t4 = 0; t4 < 2; ++t4)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(buf + TILE, lane, db, t4), dsb[t4], acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db][t4], dsb[t4], acc[db], 0, 0, 0);
   }
   if (qi < Lq) store_rows<DB>((uint16_t*)p.dq + ((int64_t)b * p.H + h) * Lq * D + (int64_t)qi * D, acc, p.scale, half);
 }
@@ -255,7 +315,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // per buffer: Q (operand order), Q (transposed), dO (operand order), dO (transposed),
   // then the tile's 32 (lse log2 e, D) pairs
   constexpr int BUF = 4 * TILE + 256;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+#ifndef BWD_DKDV_STAGES
+#define BWD_DKDV_STAGES 2
+#endif
+  constexpr int STAGES = BWD_DKDV_STAGES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -280,6 +344,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     kreg[t] = as_bf16x8(a);
     vreg[t] = as_bf16x8(c);
   }
+  settle(kreg);
+  settle(vreg);
   const float c2 = p.scale_log2;
 
   // query tiles of one head that can see any key of this block
@@ -295,7 +361,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int qt0 = (qfirst + st % per_head) * BQ;
     const uint16_t* Q = (const uint16_t*)p.q + ((int64_t)b * p.H + h) * Lq * D;
     const uint16_t* dO = (const uint16_t*)p.dout + ((int64_t)b * p.H + h) * Lq * D;
-    uint8_t* buf = smem + (st & 1) * BUF;
+    uint8_t* buf = smem + (st % STAGES) * BUF;
     load_tile<D, BPW, false>(Q, D, qt0, Lq, buf, to, wave);
     load_tile<D, BPW, true>(Q, D, qt0, Lq, buf + TILE, to, wave);
     load_tile<D, BPW, false>(dO, D, qt0, Lq, buf + 2 * TILE, to, wave);
@@ -320,27 +386,55 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     dv[i] = f32x16{};
   }
 
-  if (nsteps > 0) issue(0);
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nsteps) issue(st);
   for (int st = 0; st < nsteps; ++st) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_stage<4 * BPW, STAGES>(min(STAGES - 2, nsteps - 1 - st));
     __syncthreads();
-    if (st + 1 < nsteps) issue(st + 1);
-    const uint8_t* buf = smem + (st & 1) * BUF;
+    if (st + STAGES - 1 < nsteps) issue(st + STAGES - 1);
+    const uint8_t* buf = smem + (st % STAGES) * BUF;
     const int qt0 = (qfirst + st % per_head) * BQ;
+    // S = Q K^T and dP = dO V^T: every operand is requested before the first product
+    bf16x8 qa[DT], da[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      qa[t] = op_read(buf, lane, t);
+      da[t] = op_read(buf + 2 * TILE, lane, t);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf, lane, t), kreg[t], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(buf + 2 * TILE, lane, t), vreg[t], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], kreg[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], vreg[t], dp, 0, 0, 0);
     }
-    // P and dS for the 16 query rows of this lane's accumulator column (its key)
+    __builtin_amdgcn_sched_barrier(0);
+    // the tile's (lse log2 e, D) pairs, then the dV and dK products' operands, requested
+    // while S and dP are computed
     const float* ld = (const float*)(buf + 4 * TILE);
-    bf16x8 pb[2], dsb[2];
+    f32x4 la[4], lc[4];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int r0 = 8 * g4 + 4 * half;  // 4 consecutive query rows
-      const f32x4 a = *(const lds_f32x4*)(ld + 2 * r0);
-      const f32x4 c = *(const lds_f32x4*)(ld + 2 * r0 + 4);
+      la[g4] = *(const lds_f32x4*)(ld + 2 * r0);
+      lc[g4] = *(const lds_f32x4*)(ld + 2 * r0 + 4);
+    }
+    bf16x8 ot[DB][2], qt[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4) {
+        ot[db][t4] = tr_read(buf + 3 * TILE, lane, db, t4);
+        qt[db][t4] = tr_read(buf + TILE, lane, db, t4);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // P and dS for the 16 query rows of this lane's accumulator column (its key)
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 8 * g4 + 4 * half;
+      const f32x4 a = la[g4], c = lc[g4];
       const float l2[4] = {a.x, a.z, c.x, c.z}, dd[4] = {a.y, a.w, c.y, c.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -361,8 +455,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t4 = 0; t4 < 2; ++t4) {
-        mfma_agpr(dv[db], tr_read(buf + 3 * TILE, lane, db, t4), pb[t4]);
-        mfma_agpr(dk[db], tr_read(buf + TILE, lane, db, t4), dsb[t4]);
+        mfma_agpr(dv[db], ot[db][t4], pb[t4]);
+        mfma_agpr(dk[db], qt[db][t4], dsb[t4]);
       }
   }
   agpr_settle();
