@@ -13,7 +13,9 @@
 //    holding dQ in registers: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
 //  * bwd_dkdv_kernel owns keys (4 wavefronts x 32 keys) and streams query tiles of 32
 //    of every query head that reads its KV head, holding dK and dV in registers:
-//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
+//    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.  Each wavefront
+//    software-pipelines the tiles: the S and dP products of tile st+1 run on the matrix
+//    cores while the VALU turns tile st's S and dP into P and dS.
 // Both recompute S and P (seven tile products per pair of tiles instead of five) so
 // that every gradient is written exactly once.
 //
@@ -34,6 +36,7 @@ constexpr float kLog2e = 1.4426950408889634074f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;  // byte address in LDS
 
 // Byte offsets of one wavefront's 1 KiB direct-to-LDS blocks of a [R rows, D] tile
 // (R = 32): "operand order" (block (t): rows lane % 32, 16-byte chunk 2t + lane / 32) and
@@ -69,16 +72,33 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, int64_t rs, int 
   }
 }
 
-// A operand of k-step t from an operand-order tile (16 bytes per lane)
-__device__ __forceinline__ bf16x8 op_read(const uint8_t* tile, int lane, int t) {
-  return as_bf16x8(*(const lds_u32x4*)(tile + lane * 16 + t * 1024));
+// LDS reads at a per-lane byte address plus a compile-time offset.  The per-lane base
+// (stage + lane offset) is formed once per tile and passed through an empty asm
+// statement, so that the compiler keeps one base register and folds every constant into
+// the instruction's offset field instead of re-deriving each address.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const lds_void*)p;
+}
+__device__ __forceinline__ unsigned opaque(unsigned a) {
+  asm volatile("" : "+v"(a));
+  return a;
+}
+__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
+
+// Lane offsets: operand-order A operand (16 bytes per lane) and the transposing reads.
+__device__ __forceinline__ unsigned op_lane(int lane) { return (unsigned)lane * 16u; }
+__device__ __forceinline__ unsigned tr_lane(int lane) {
+  return (unsigned)((4 * (lane >> 5) + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+}
+// A operand of k-step t from an operand-order tile; `base` = tile address + op_lane
+__device__ __forceinline__ bf16x8 op_read(unsigned base, int t) {
+  return as_bf16x8(*(const lds_u32x4*)lds_at(base + t * 1024));
 }
 // Transposed A operand (columns 32 db .. 32 db + 31, rows in accumulator order for the
-// 16-row group t4) from a transposed tile: two ds_read_b64_tr_b16
-__device__ __forceinline__ bf16x8 tr_read(const uint8_t* tile, int lane, int db, int t4) {
-  const int half = lane >> 5;
-  const int off = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-  const uint8_t* p = tile + off + db * 2048 + t4 * 1024;
+// 16-row group t4) from a transposed tile: two ds_read_b64_tr_b16; `base` = tile
+// address + tr_lane
+__device__ __forceinline__ bf16x8 tr_read(unsigned base, int db, int t4) {
+  const lds_u8* p = lds_at(base + db * 2048 + t4 * 1024);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 512));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -121,6 +141,35 @@ template <int N>
 __device__ __forceinline__ void settle(bf16x8 (&r)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// Four 1 KiB direct-to-LDS blocks from one M0 write: the instruction offset i * 1024
+// moves both the memory address and the LDS destination of block i (the 12-bit field
+// reaches block 3), so the per-lane memory offsets passed in have i * 1024 taken out,
+// biased by kDmaBias (the descriptor's base sits that many bytes before the tile).  The
+// wait states after the M0 write and after SGPR writes by VALU are spelled out, as the
+// hazard recognizer does not see inside the asm.
+constexpr int kDmaBias = 4096;
+__device__ __forceinline__ void dma4(u32x4s r, unsigned m0, int v0, int v1, int v2, int v3) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\t"
+               "buffer_load_dwordx4 %2, %1, 0 offen lds\n\t"
+               "buffer_load_dwordx4 %3, %1, 0 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %4, %1, 0 offen offset:2048 lds\n\t"
+               "buffer_load_dwordx4 %5, %1, 0 offen offset:3072 lds"
+               :
+               : "s"(m0), "s"(r), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+               : "memory", "m0");
+}
+// Descriptor over [base - kDmaBias, +2 GiB): every row read is a valid one (the last
+// tile's rows are clamped), so the range is not used as a guard.
+__device__ __forceinline__ u32x4s biased_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)base - kDmaBias;
+  u32x4s r;
+  r.x = (unsigned)a;
+  r.y = (unsigned)(a >> 32) & 0xFFFFu;
+  r.z = 0x7FFFFFFFu;
+  r.w = 0x00020000u;
+  return r;
 }
 
 // Tiles stream through a ring of STAGES LDS buffers, STAGES - 1 ahead of use.  Before
@@ -177,10 +226,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int TILE = BN * D * 2;          // bytes of one [32, D] bf16 tile
   constexpr int BPW = TILE / 1024 / NW;     // 1 KiB blocks per wavefront per tile
   static_assert(BPW * NW * 1024 == TILE, "tile split");
-#ifndef BWD_DQ_STAGES
-#define BWD_DQ_STAGES 2
-#endif
-  constexpr int STAGES = BWD_DQ_STAGES;
+  constexpr int STAGES = 2;  // deeper rings measured no faster
   // per stage: K (operand order), K (transposed), V (operand order)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 3 * TILE];
 
@@ -247,22 +293,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     wait_stage<3 * BPW, STAGES>(min(STAGES - 2, ntiles - 1 - j));  // this wave's share of tile j
     __syncthreads();  // ... and every wave's; the stage of tile j-1 is free
     if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
-    const uint8_t* buf = smem + (j % STAGES) * 3 * TILE;
+    const unsigned sbase = lds_addr(smem) + (unsigned)((j % STAGES) * 3 * TILE);
+    const unsigned ob = opaque(sbase + op_lane(lane)), tb = opaque(sbase + tr_lane(lane));
     // S^T = K Q^T and dP^T = V dO^T, operands read KPF k-steps ahead of their products
     constexpr int KPF = 3;
     bf16x8 ka[KPF], va[KPF];
 #pragma unroll
     for (int u = 0; u < KPF; ++u) {
-      ka[u] = op_read(buf, lane, u);
-      va[u] = op_read(buf + 2 * TILE, lane, u);
+      ka[u] = op_read(ob, u);
+      va[u] = op_read(ob + 2 * TILE, u);
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       bf16x8 kn = ka[t % KPF], vn = va[t % KPF];
       if (t + KPF < DT) {
-        kn = op_read(buf, lane, t + KPF);
-        vn = op_read(buf + 2 * TILE, lane, t + KPF);
+        kn = op_read(ob, t + KPF);
+        vn = op_read(ob + 2 * TILE, t + KPF);
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % KPF], qreg[t], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % KPF], dreg[t], dp, 0, 0, 0);
@@ -275,7 +322,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = tr_read(buf + TILE, lane, db, t4);
+      for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = tr_read(tb + TILE, db, t4);
     __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); keys past the end or above the diagonal have P = 0
     const int base = j * BN + 4 * half;
@@ -310,15 +357,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int NW = 4, BK = 32 * NW, BQ = 32;
   constexpr int DT = D / 16, DB = D / 32;
   constexpr int TILE = BQ * D * 2;
-  constexpr int BPW = TILE / 1024 / NW;
-  static_assert(BPW * NW * 1024 == TILE, "tile split");
   // per buffer: Q (operand order), Q (transposed), dO (operand order), dO (transposed),
   // then the tile's 32 (lse log2 e, D) pairs
   constexpr int BUF = 4 * TILE + 256;
-#ifndef BWD_DKDV_STAGES
-#define BWD_DKDV_STAGES 2
-#endif
-  constexpr int STAGES = BWD_DKDV_STAGES;
+  constexpr int STAGES = 3;  // tiles st (phase 2), st+1 (phase 1) and st+2 (loading)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -354,28 +396,55 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int per_head = max(0, nqt - qfirst);
   const int nsteps = G * per_head;
 
-  TileOffsets<D, BPW> to;
-  to.init(wave, lane);
-  auto issue = [&](int st) {
-    const int h = hk * G + st / per_head;
-    const int qt0 = (qfirst + st % per_head) * BQ;
-    const uint16_t* Q = (const uint16_t*)p.q + ((int64_t)b * p.H + h) * Lq * D;
-    const uint16_t* dO = (const uint16_t*)p.dout + ((int64_t)b * p.H + h) * Lq * D;
-    uint8_t* buf = smem + (st % STAGES) * BUF;
-    load_tile<D, BPW, false>(Q, D, qt0, Lq, buf, to, wave);
-    load_tile<D, BPW, true>(Q, D, qt0, Lq, buf + TILE, to, wave);
-    load_tile<D, BPW, false>(dO, D, qt0, Lq, buf + 2 * TILE, to, wave);
-    load_tile<D, BPW, true>(dO, D, qt0, Lq, buf + 3 * TILE, to, wave);
+  const unsigned lsm = lds_addr(smem);
+  // DMA: wavefront w streams layout w of every tile (0: Q in operand order, 1: Q
+  // transposed, 2: dO in operand order, 3: dO transposed), NB 1 KiB blocks each, through
+  // one descriptor; wavefront 0 also brings the tile's 32 (lse log2 e, D) pairs.  Block
+  // i of a layout: operand order = rows lane % 32, 16-byte chunk 2 i + lane / 32;
+  // transposed = rows 16 (i % 2) + lane / 4, chunk 4 (i / 2) + lane % 4.
+  constexpr int NB = TILE / 1024;
+  static_assert(NB % 4 == 0, "whole groups of four blocks");
+  const bool trl = (wave & 1) != 0;
+  int brow[NB], bcol[NB], voff[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    brow[i] = trl ? 16 * (i & 1) + lane / 4 : (lane & 31);
+    bcol[i] = trl ? (32 * (i >> 1) + 8 * (lane & 3)) * 2 : (2 * i + (lane >> 5)) * 16;
+    voff[i] = brow[i] * (D * 2) + bcol[i] - (i & 3) * 1024 + kDmaBias;
+  }
+  const uint16_t* const src0 = (const uint16_t*)((wave >> 1) ? p.dout : p.q) + ((int64_t)b * p.H + hk * G) * Lq * D;
+  const float* const ws0 = p.ws + 2 * ((int64_t)b * p.H + hk * G) * Lq;
+  // cursors: the next tile to load (head of the group, query tile) and its ring stage
+  int ld_h = 0, ld_t = qfirst, ld_s = 0;
+  auto issue = [&]() {
+    const int qt0 = ld_t * BQ;
+    const int last = Lq - qt0 - 1;  // last valid row of the tile (>= 0)
+    const u32x4s r = biased_rsrc(src0 + ((int64_t)ld_h * Lq + qt0) * D);
+    const unsigned m0 = lsm + (unsigned)(ld_s * BUF + wave * TILE);
+    if (last >= BQ - 1) {
+#pragma unroll
+      for (int g = 0; g < NB; g += 4)
+        dma4(r, m0 + g * 1024, voff[g], voff[g + 1], voff[g + 2], voff[g + 3]);
+    } else {
+      int vo[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) vo[i] = min(brow[i], last) * (D * 2) + bcol[i] - (i & 3) * 1024 + kDmaBias;
+#pragma unroll
+      for (int g = 0; g < NB; g += 4) dma4(r, m0 + g * 1024, vo[g], vo[g + 1], vo[g + 2], vo[g + 3]);
+    }
     if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i
-      const int last = Lq - qt0 - 1;
-      const float* ws = p.ws + 2 * (((int64_t)b * p.H + h) * Lq + qt0);
-      const u32x4s r = buffer_rsrc(ws, ((int64_t)last + 1) * 8);
-      const int voff = min(lane >> 1, last) * 8 + (lane & 1) * 4;
-      const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)(buf + 4 * TILE));
+      const float* ws = ws0 + 2 * ((int64_t)ld_h * Lq + qt0);
+      const u32x4s pr = buffer_rsrc(ws, ((int64_t)last + 1) * 8);
+      const int pv = min(lane >> 1, last) * 8 + (lane & 1) * 4;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :
-                   : "s"(m0v), "v"(voff), "s"(r)
+                   : "s"(m0 + (unsigned)(4 * TILE - wave * TILE)), "v"(pv), "s"(pr)
                    : "memory", "m0");
+    }
+    ld_s = ld_s + 1 == STAGES ? 0 : ld_s + 1;
+    if (++ld_t == nqt) {
+      ld_t = qfirst;
+      ++ld_h;
     }
   };
 
@@ -386,79 +455,129 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     dv[i] = f32x16{};
   }
 
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nsteps) issue(st);
-  for (int st = 0; st < nsteps; ++st) {
-    wait_stage<4 * BPW, STAGES>(min(STAGES - 2, nsteps - 1 - st));
-    __syncthreads();
-    if (st + STAGES - 1 < nsteps) issue(st + STAGES - 1);
-    const uint8_t* buf = smem + (st % STAGES) * BUF;
-    const int qt0 = (qfirst + st % per_head) * BQ;
-    // S = Q K^T and dP = dO V^T: every operand is requested before the first product
-    bf16x8 qa[DT], da[DT];
+  auto products = [&](f32x16& s, f32x16& dp) {  // S, dP of the first tile (stage 0)
+    const unsigned ob = opaque(lsm + op_lane(lane));
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      qa[t] = op_read(buf, lane, t);
-      da[t] = op_read(buf + 2 * TILE, lane, t);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(ob, t), kreg[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(ob + 2 * TILE, t), vreg[t], dp, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s = f32x16{}, dp = f32x16{};
+  };
+  // Admissible query rows of this lane's key: q in [qlo, Lq), none when key >= Lk.  A
+  // row q is admissible iff (unsigned)(q - qlo) < span.
+  const int qlo = CAUSAL ? key - shift : 0;
+  const unsigned span = key < Lk ? (unsigned)max(0, Lq - qlo) : 0u;
+  constexpr int KPF = 2;               // k-steps of S / dP operands in flight
+  constexpr int EPK = 16 / DT;         // P / dS elements per k-step (2 at d = 128)
+  constexpr int PPK = EPK / 2;         // (lse, D) 16-byte reads per k-step
+  constexpr int NTR = 4 * DB;          // dV / dK operands (two transposing reads each)
+  constexpr int TPK = NTR / DT;        // of them requested per k-step of the second half
+  // the 16-byte (lse log2 e, D) pair read pp of a tile: rows 8 (pp / 2) + 4 half + 2 (pp % 2) + {0, 1}
+  // (`base` = stage address + 32 half)
+  auto pair_read = [&](unsigned base, int pp) -> f32x4 {
+    return *(const lds_f32x4*)lds_at(base + 4 * TILE + (16 * (pp >> 1) + 4 * (pp & 1)) * 4);
+  };
+  int c_s = 0, c_t = qfirst;  // ring stage and query tile of the tile being finished
+  auto step = [&](int st, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
+    wait_stage<NB, STAGES - 1>(min(STAGES - 3, nsteps - 2 - st));  // tile st+1 landed
+    __syncthreads();  // ... for every wave; the stage of tile st-1 is free
+    if (st + STAGES - 1 < nsteps) issue();
+    const int c_n = c_s + 1 == STAGES ? 0 : c_s + 1;  // stage of tile st+1
+    const unsigned cst = lsm + (unsigned)(c_s * BUF);
+    const unsigned nst = lsm + (unsigned)(c_n * BUF);
+    const unsigned ob = opaque(nst + op_lane(lane));    // operand reads of tile st+1
+    const unsigned tb = opaque(cst + tr_lane(lane));    // transposing reads of tile st
+    const unsigned lb = opaque(cst + 32u * half);       // (lse, D) pairs of tile st
+    const int qt0 = c_t * BQ;
+    c_s = c_n;  // the cursors move on to tile st+1
+    if (++c_t == nqt) c_t = qfirst;
+    const int d0 = qt0 + 4 * half - qlo;  // (q - qlo) of accumulator row 0 of this lane
+    bf16x8 qa[KPF], da[KPF];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], kreg[t], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], vreg[t], dp, 0, 0, 0);
+    for (int u = 0; u < KPF; ++u) {
+      qa[u] = op_read(ob, u);
+      da[u] = op_read(ob + 2 * TILE, u);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // the tile's (lse log2 e, D) pairs, then the dV and dK products' operands, requested
-    // while S and dP are computed
-    const float* ld = (const float*)(buf + 4 * TILE);
-    f32x4 la[4], lc[4];
+    f32x4 lp[PPK];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = 8 * g4 + 4 * half;  // 4 consecutive query rows
-      la[g4] = *(const lds_f32x4*)(ld + 2 * r0);
-      lc[g4] = *(const lds_f32x4*)(ld + 2 * r0 + 4);
-    }
-    bf16x8 ot[DB][2], qt[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int t4 = 0; t4 < 2; ++t4) {
-        ot[db][t4] = tr_read(buf + 3 * TILE, lane, db, t4);
-        qt[db][t4] = tr_read(buf + TILE, lane, db, t4);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // P and dS for the 16 query rows of this lane's accumulator column (its key)
+    for (int i = 0; i < PPK; ++i) lp[i] = pair_read(lb, i);
+    bf16x8 trop[NTR];  // operand 4 db + 2 t4 + 0: dO^T, + 1: Q^T
     bf16x8 pb[2], dsb[2];
+    sn = f32x16{};
+    dpn = f32x16{};
+    // phase 1: S, dP of tile st+1; P, dS of tile st
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = 8 * g4 + 4 * half;
-      const f32x4 a = la[g4], c = lc[g4];
-      const float l2[4] = {a.x, a.z, c.x, c.z}, dd[4] = {a.y, a.w, c.y, c.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * g4 + e;
-        const int q = qt0 + r0 + e;
-        const bool ok = q < Lq && key < Lk && (!CAUSAL || key <= q + shift);
-        const float pv = ok ? exp2_fast(__builtin_fmaf(s[v], c2, -l2[e])) : 0.f;
-        pb[v >> 3][v & 7] = (__bf16)pv;
-        dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dd[e]));
+    for (int t = 0; t < DT; ++t) {
+      bf16x8 qn = qa[t % KPF], dn = da[t % KPF];
+      if (t + KPF < DT) {
+        qn = op_read(ob, t + KPF);
+        dn = op_read(ob + 2 * TILE, t + KPF);
       }
+      f32x4 ln[PPK];
+#pragma unroll
+      for (int i = 0; i < PPK; ++i) ln[i] = (t + 1 < DT) ? pair_read(lb, (t + 1) * PPK + i) : lp[i];
+      if (t >= DT / 2) {  // the first half of the phase-2 operands
+#pragma unroll
+        for (int i = 0; i < TPK; ++i) {
+          const int idx = (t - DT / 2) * TPK + i;
+          trop[idx] = tr_read(tb + ((idx & 1) ? TILE : 3 * TILE), idx >> 2, (idx >> 1) & 1);
+        }
+      }
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % KPF], kreg[t], sn, 0, 0, 0);
+      dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t % KPF], vreg[t], dpn, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EPK; ++e) {
+        const int v = t * EPK + e;
+        const f32x4 pr = lp[e >> 1];
+        const float l2 = (v & 1) ? pr.z : pr.x, dd = (v & 1) ? pr.w : pr.y;
+        const bool ok = (unsigned)(d0 + acc_row(v, 0)) < span;
+        const float x = ok ? __builtin_fmaf(sc[v], c2, -l2) : kNegInf;  // exp2(-inf) = 0
+        const float pv = exp2_fast(x);
+        pb[v >> 3][v & 7] = (__bf16)pv;
+        dsb[v >> 3][v & 7] = (__bf16)(pv * (dpc[v] - dd));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      qa[t % KPF] = qn;
+      da[t % KPF] = dn;
+#pragma unroll
+      for (int i = 0; i < PPK; ++i) lp[i] = ln[i];
     }
+    // the second half of the phase-2 operands
+#pragma unroll
+    for (int idx = NTR / 2; idx < NTR; ++idx)
+      trop[idx] = tr_read(tb + ((idx & 1) ? TILE : 3 * TILE), idx >> 2, (idx >> 1) & 1);
     // The asm MFMAs below read P and dS, just written by VALU: the hazard recognizer does
     // not see them, so five wait states are spelled out here, after the last write (the
     // operands are tied to this statement so that no write can move past it).
     asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]), "+v"(dsb[0]), "+v"(dsb[1]));
-    // dV^T += dO^T P,  dK^T += Q^T dS
+    // phase 2: dV^T += dO^T P,  dK^T += Q^T dS
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t4 = 0; t4 < 2; ++t4) {
-        mfma_agpr(dv[db], ot[db][t4], pb[t4]);
-        mfma_agpr(dk[db], qt[db][t4], dsb[t4]);
+        mfma_agpr(dv[db], trop[4 * db + 2 * t4], pb[t4]);
+        mfma_agpr(dk[db], trop[4 * db + 2 * t4 + 1], dsb[t4]);
       }
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nsteps) issue();
+  f32x16 sA, dA, sB, dB;
+  if (nsteps > 0) {
+    wait_stage<NB, STAGES>(min(STAGES - 2, nsteps - 1));  // tile 0 landed
+    __syncthreads();
+    products(sA, dA);
   }
+  // unrolled by two so that the two S / dP sets swap roles without copies
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, sA, dA, sB, dB);
+    step(st + 1, sB, dB, sA, dA);
+  }
+  if (st < nsteps) step(st, sA, dA, sB, dB);
   agpr_settle();
   if (key < Lk) {
     const int64_t row = ((int64_t)b * p.H_kv + hk) * Lk * D + (int64_t)key * D;
