@@ -24,8 +24,8 @@
 // 16 rows; the bf16 P or dS feeds the next product as the B operand straight from the
 // accumulator, and the A operand of that product (K^T, dO^T, Q^T) is read from LDS with
 // transposing reads in the accumulator's row order.  Tiles go global -> LDS with
-// direct-to-LDS loads, each tensor in the layout its product needs ("operand order" for
-// A operands read 16 bytes per lane, "transposed" for the ds_read_b64_tr_b16 operands).
+// direct-to-LDS loads into one swizzled layout per tensor that serves both the 16-byte
+// operand reads and the ds_read_b64_tr_b16 transposing reads without bank conflicts.
 #include "attn_internal.h"
 #include "attn_tile.h"
 
@@ -37,40 +37,6 @@ constexpr float kLog2e = 1.4426950408889634074f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;  // byte address in LDS
-
-// Byte offsets of one wavefront's 1 KiB direct-to-LDS blocks of a [R rows, D] tile
-// (R = 32): "operand order" (block (t): rows lane % 32, 16-byte chunk 2t + lane / 32) and
-// "transposed" (block (db, r16): rows 16 r16 + lane / 4, chunk 4 db + lane % 4).
-template <int D, int BPW>
-struct TileOffsets {
-  int orow[BPW], ocol[BPW], trow[BPW], tcol[BPW];
-  __device__ void init(int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int bi = wave * BPW + i;
-      orow[i] = lane & 31;
-      ocol[i] = (2 * bi + (lane >> 5)) * 16;
-      trow[i] = 16 * (bi & 1) + lane / 4;
-      tcol[i] = (32 * (bi >> 1) + 8 * (lane % 4)) * 2;
-    }
-  }
-};
-
-// Load rows [r0, r0 + 32) of a row-major tensor (row stride `rs` elements) into an LDS
-// tile in operand order (TR = false) or transposed order (TR = true); rows at or past
-// `nrows` are clamped to the last row (they are masked by the caller).
-template <int D, int BPW, bool TR>
-__device__ __forceinline__ void load_tile(const uint16_t* base, int64_t rs, int r0, int nrows, uint8_t* lds,
-                                          const TileOffsets<D, BPW>& to, int wave) {
-  const int last = nrows - r0 - 1;  // >= 0
-  const u32x4s r = buffer_rsrc(base + (int64_t)r0 * rs, ((int64_t)last * rs + D) * 2);
-  const int rbytes = (int)rs * 2;
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int row = min(TR ? to.trow[i] : to.orow[i], last);
-    dma16(r, lds + (wave * BPW + i) * 1024, row * rbytes + (TR ? to.tcol[i] : to.ocol[i]));
-  }
-}
 
 // LDS reads at a per-lane byte address plus a compile-time offset.  The per-lane base
 // (stage + lane offset) is formed once per tile and passed through an empty asm
@@ -85,23 +51,32 @@ __device__ __forceinline__ unsigned opaque(unsigned a) {
 }
 __device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
 
-// Lane offsets: operand-order A operand (16 bytes per lane) and the transposing reads.
-__device__ __forceinline__ unsigned op_lane(int lane) { return (unsigned)lane * 16u; }
-__device__ __forceinline__ unsigned tr_lane(int lane) {
-  return (unsigned)((4 * (lane >> 5) + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+// Swizzled [32 rows, D] bf16 tile serving both read patterns without bank conflicts:
+// 16-byte chunk c (columns 8 c .. 8 c + 7) of row r sits at c * 512 + (r ^ 4 (c % 4)) * 16.
+// Operand-order A operand of k-step t: lane l reads chunk 2 t + l / 32 of row l % 32,
+// at sw_op_lane(l, t % 2) + 1024 t.
+__device__ __forceinline__ unsigned sw_op_lane(int lane, int parity) {
+  const int half = lane >> 5;
+  return (unsigned)(half * 512 + (((lane & 31) ^ (4 * half) ^ (8 * parity)) * 16));
 }
-// A operand of k-step t from an operand-order tile; `base` = tile address + op_lane
+// Transposing reads: lane l reads 8 bytes of chunk 4 db + j of row 16 t4 + x (first
+// read) and row 16 t4 + x + 8 (second), with x = 4 (l / 32) + (l % 16) / 4 and
+// j = 2 ((l / 16) % 2) + (l % 4) / 2, byte 8 (l % 2) of the chunk.
+__device__ __forceinline__ unsigned sw_tr_lane(int lane, int second) {
+  const int x = 4 * (lane >> 5) + (lane & 15) / 4;
+  const int j = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  return (unsigned)(j * 512 + (((x ^ (4 * j)) ^ (8 * second)) * 16) + 8 * (lane & 1));
+}
+__device__ __forceinline__ bf16x8 sw_tr_read(unsigned lo_base, unsigned hi_base, int db, int t4) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(lo_base + db * 2048 + t4 * 256));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(hi_base + db * 2048 + t4 * 256));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Operand-order A operand of k-step t from a swizzled tile; `base` = tile address +
+// sw_op_lane(lane, t % 2)
 __device__ __forceinline__ bf16x8 op_read(unsigned base, int t) {
   return as_bf16x8(*(const lds_u32x4*)lds_at(base + t * 1024));
-}
-// Transposed A operand (columns 32 db .. 32 db + 31, rows in accumulator order for the
-// 16-row group t4) from a transposed tile: two ds_read_b64_tr_b16; `base` = tile
-// address + tr_lane
-__device__ __forceinline__ bf16x8 tr_read(unsigned base, int db, int t4) {
-  const lds_u8* p = lds_at(base + db * 2048 + t4 * 1024);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 512));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // Accumulator element v of lane (half = lane / 32) sits in row 8 (v / 4) + 4 half + v % 4.
@@ -172,6 +147,46 @@ __device__ __forceinline__ u32x4s biased_rsrc(const void* base) {
   return r;
 }
 
+// Direct-to-LDS loads of two [32, D] bf16 tiles (tensor 0 then tensor 1, each
+// TILE bytes) into the swizzled layout (sw_op_lane): 2 NB 1 KiB blocks, wavefront
+// w < NWU carrying blocks 4 w .. 4 w + 3, which all belong to one tensor.  Block i of a
+// tile holds chunks 2 i and 2 i + 1 of every row: lane l carries chunk c = 2 i + l / 32
+// of row (l % 32) ^ 4 (c % 4).
+template <int D>
+struct TilePairDma {
+  static constexpr int TILE = 32 * D * 2, NB = TILE / 1024, NWU = NB / 2;
+  static_assert(NB % 4 == 0, "whole groups of four blocks");
+  int tsr;  // tensor of this wavefront's blocks
+  int brow[4], bcol[4], voff[4];
+  __device__ void init(int wave, int lane) {
+    tsr = min(1, 4 * wave / NB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 2 * ((4 * wave + i) % NB) + (lane >> 5);
+      brow[i] = (lane & 31) ^ (4 * (c & 3));
+      bcol[i] = c * 16;
+      voff[i] = brow[i] * (D * 2) + bcol[i] - i * 1024 + kDmaBias;
+    }
+  }
+  // rows [r0, r0 + 32) of this wavefront's tensor (row-major, row stride D, `nrows`
+  // valid rows: later rows are clamped to the last one) into the stage at LDS byte
+  // address `stage`
+  __device__ void issue(const uint16_t* src, int r0, int nrows, unsigned stage, int wave) const {
+    if (wave >= NWU) return;
+    const int last = nrows - r0 - 1;  // >= 0
+    const u32x4s r = biased_rsrc(src + (int64_t)r0 * D);
+    const unsigned m0 = stage + (unsigned)(wave * 4096);
+    if (last >= 31) {
+      dma4(r, m0, voff[0], voff[1], voff[2], voff[3]);
+    } else {
+      int vo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vo[i] = min(brow[i], last) * (D * 2) + bcol[i] - i * 1024 + kDmaBias;
+      dma4(r, m0, vo[0], vo[1], vo[2], vo[3]);
+    }
+  }
+};
+
 // Tiles stream through a ring of STAGES LDS buffers, STAGES - 1 ahead of use.  Before
 // using a stage, a wavefront waits for its own L direct-to-LDS loads of that stage while
 // up to `later` (<= STAGES - 2) younger stages stay in flight: loads complete in issue
@@ -224,11 +239,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NW = 4, BM = 32 * NW, BN = 32;
   constexpr int DT = D / 16, DB = D / 32;
   constexpr int TILE = BN * D * 2;          // bytes of one [32, D] bf16 tile
-  constexpr int BPW = TILE / 1024 / NW;     // 1 KiB blocks per wavefront per tile
-  static_assert(BPW * NW * 1024 == TILE, "tile split");
   constexpr int STAGES = 2;  // deeper rings measured no faster
-  // per stage: K (operand order), K (transposed), V (operand order)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 3 * TILE];
+  // per stage: the K tile and the V tile, swizzled (sw_op_lane)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,14 +286,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   asm volatile("" : "+v"(lse2), "+v"(dsum));
   const float c2 = p.scale_log2;
 
-  TileOffsets<D, BPW> to;
-  to.init(wave, lane);
-  auto issue = [&](int j) {
-    uint8_t* buf = smem + (j % STAGES) * 3 * TILE;
-    load_tile<D, BPW, false>(K, D, j * BN, Lk, buf, to, wave);
-    load_tile<D, BPW, true>(K, D, j * BN, Lk, buf + TILE, to, wave);
-    load_tile<D, BPW, false>(V, D, j * BN, Lk, buf + 2 * TILE, to, wave);
-  };
+  const unsigned lsm = lds_addr(smem);
+  TilePairDma<D> dma;
+  dma.init(wave, lane);
+  const uint16_t* const src = dma.tsr ? V : K;
+  auto issue = [&](int j) { dma.issue(src, j * BN, Lk, lsm + (unsigned)((j % STAGES) * 2 * TILE), wave); };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -290,26 +300,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int j = 0; j < STAGES - 1; ++j)
     if (j < ntiles) issue(j);
   for (int j = 0; j < ntiles; ++j) {
-    wait_stage<3 * BPW, STAGES>(min(STAGES - 2, ntiles - 1 - j));  // this wave's share of tile j
+    wait_stage<4, STAGES>(min(STAGES - 2, ntiles - 1 - j));  // this wave's share of tile j
     __syncthreads();  // ... and every wave's; the stage of tile j-1 is free
     if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
-    const unsigned sbase = lds_addr(smem) + (unsigned)((j % STAGES) * 3 * TILE);
-    const unsigned ob = opaque(sbase + op_lane(lane)), tb = opaque(sbase + tr_lane(lane));
+    const unsigned sbase = lsm + (unsigned)((j % STAGES) * 2 * TILE);
+    const unsigned o0 = opaque(sbase + sw_op_lane(lane, 0)), o1 = opaque(sbase + sw_op_lane(lane, 1));
+    const unsigned t0 = opaque(sbase + sw_tr_lane(lane, 0)), t1 = opaque(sbase + sw_tr_lane(lane, 1));
     // S^T = K Q^T and dP^T = V dO^T, operands read KPF k-steps ahead of their products
     constexpr int KPF = 3;
     bf16x8 ka[KPF], va[KPF];
 #pragma unroll
     for (int u = 0; u < KPF; ++u) {
-      ka[u] = op_read(ob, u);
-      va[u] = op_read(ob + 2 * TILE, u);
+      ka[u] = op_read((u & 1) ? o1 : o0, u);
+      va[u] = op_read(((u & 1) ? o1 : o0) + TILE, u);
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       bf16x8 kn = ka[t % KPF], vn = va[t % KPF];
       if (t + KPF < DT) {
-        kn = op_read(ob, t + KPF);
-        vn = op_read(ob + 2 * TILE, t + KPF);
+        kn = op_read(((t + KPF) & 1) ? o1 : o0, t + KPF);
+        vn = op_read((((t + KPF) & 1) ? o1 : o0) + TILE, t + KPF);
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % KPF], qreg[t], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % KPF], dreg[t], dp, 0, 0, 0);
@@ -322,7 +333,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = tr_read(tb + TILE, db, t4);
+      for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = sw_tr_read(t0, t1, db, t4);
     __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); keys past the end or above the diagonal have P = 0
     const int base = j * BN + 4 * half;
@@ -335,7 +346,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int off = 8 * (v >> 2) + (v & 3);
-      const float pv = off <= lim ? exp2_fast(__builtin_fmaf(s[v], c2, -lse2)) : 0.f;
+      const float pv = exp2_fast(off <= lim ? __builtin_fmaf(s[v], c2, -lse2) : kNegInf);  // exp2(-inf) = 0
       dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dsum));
     }
     // dQ^T += K^T dS^T
@@ -357,9 +368,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int NW = 4, BK = 32 * NW, BQ = 32;
   constexpr int DT = D / 16, DB = D / 32;
   constexpr int TILE = BQ * D * 2;
-  // per buffer: Q (operand order), Q (transposed), dO (operand order), dO (transposed),
-  // then the tile's 32 (lse log2 e, D) pairs
-  constexpr int BUF = 4 * TILE + 256;
+  // per stage: the Q tile, the dO tile (swizzled layout, see sw_op_lane), then the
+  // tile's 32 (lse log2 e, D) pairs
+  constexpr int BUF = 2 * TILE + 256;
   constexpr int STAGES = 3;  // tiles st (phase 2), st+1 (phase 1) and st+2 (loading)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF];
 
@@ -397,48 +408,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nsteps = G * per_head;
 
   const unsigned lsm = lds_addr(smem);
-  // DMA: wavefront w streams layout w of every tile (0: Q in operand order, 1: Q
-  // transposed, 2: dO in operand order, 3: dO transposed), NB 1 KiB blocks each, through
-  // one descriptor; wavefront 0 also brings the tile's 32 (lse log2 e, D) pairs.  Block
-  // i of a layout: operand order = rows lane % 32, 16-byte chunk 2 i + lane / 32;
-  // transposed = rows 16 (i % 2) + lane / 4, chunk 4 (i / 2) + lane % 4.
-  constexpr int NB = TILE / 1024;
-  static_assert(NB % 4 == 0, "whole groups of four blocks");
-  const bool trl = (wave & 1) != 0;
-  int brow[NB], bcol[NB], voff[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    brow[i] = trl ? 16 * (i & 1) + lane / 4 : (lane & 31);
-    bcol[i] = trl ? (32 * (i >> 1) + 8 * (lane & 3)) * 2 : (2 * i + (lane >> 5)) * 16;
-    voff[i] = brow[i] * (D * 2) + bcol[i] - (i & 3) * 1024 + kDmaBias;
-  }
-  const uint16_t* const src0 = (const uint16_t*)((wave >> 1) ? p.dout : p.q) + ((int64_t)b * p.H + hk * G) * Lq * D;
+  // DMA: the Q and dO tiles through TilePairDma; wavefront 0 also brings the tile's 32
+  // (lse log2 e, D) pairs
+  TilePairDma<D> dma;
+  dma.init(wave, lane);
+  const uint16_t* const src0 = (const uint16_t*)(dma.tsr ? p.dout : p.q) + ((int64_t)b * p.H + hk * G) * Lq * D;
   const float* const ws0 = p.ws + 2 * ((int64_t)b * p.H + hk * G) * Lq;
   // cursors: the next tile to load (head of the group, query tile) and its ring stage
   int ld_h = 0, ld_t = qfirst, ld_s = 0;
   auto issue = [&]() {
     const int qt0 = ld_t * BQ;
     const int last = Lq - qt0 - 1;  // last valid row of the tile (>= 0)
-    const u32x4s r = biased_rsrc(src0 + ((int64_t)ld_h * Lq + qt0) * D);
-    const unsigned m0 = lsm + (unsigned)(ld_s * BUF + wave * TILE);
-    if (last >= BQ - 1) {
-#pragma unroll
-      for (int g = 0; g < NB; g += 4)
-        dma4(r, m0 + g * 1024, voff[g], voff[g + 1], voff[g + 2], voff[g + 3]);
-    } else {
-      int vo[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) vo[i] = min(brow[i], last) * (D * 2) + bcol[i] - (i & 3) * 1024 + kDmaBias;
-#pragma unroll
-      for (int g = 0; g < NB; g += 4) dma4(r, m0 + g * 1024, vo[g], vo[g + 1], vo[g + 2], vo[g + 3]);
-    }
+    dma.issue(src0 + (int64_t)ld_h * Lq * D, qt0, Lq, lsm + (unsigned)(ld_s * BUF), wave);
     if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i
       const float* ws = ws0 + 2 * ((int64_t)ld_h * Lq + qt0);
       const u32x4s pr = buffer_rsrc(ws, ((int64_t)last + 1) * 8);
       const int pv = min(lane >> 1, last) * 8 + (lane & 1) * 4;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :
-                   : "s"(m0 + (unsigned)(4 * TILE - wave * TILE)), "v"(pv), "s"(pr)
+                   : "s"(lsm + (unsigned)(ld_s * BUF + 2 * TILE)), "v"(pv), "s"(pr)
                    : "memory", "m0");
     }
     ld_s = ld_s + 1 == STAGES ? 0 : ld_s + 1;
@@ -456,13 +444,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 
   auto products = [&](f32x16& s, f32x16& dp) {  // S, dP of the first tile (stage 0)
-    const unsigned ob = opaque(lsm + op_lane(lane));
+    const unsigned o0 = opaque(lsm + sw_op_lane(lane, 0)), o1 = opaque(lsm + sw_op_lane(lane, 1));
     s = f32x16{};
     dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
+      const unsigned ob = (t & 1) ? o1 : o0;
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(ob, t), kreg[t], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(ob + 2 * TILE, t), vreg[t], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op_read(ob + TILE, t), vreg[t], dp, 0, 0, 0);
     }
   };
   // Admissible query rows of this lane's key: q in [qlo, Lq), none when key >= Lk.  A
@@ -477,19 +466,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // the 16-byte (lse log2 e, D) pair read pp of a tile: rows 8 (pp / 2) + 4 half + 2 (pp % 2) + {0, 1}
   // (`base` = stage address + 32 half)
   auto pair_read = [&](unsigned base, int pp) -> f32x4 {
-    return *(const lds_f32x4*)lds_at(base + 4 * TILE + (16 * (pp >> 1) + 4 * (pp & 1)) * 4);
+    return *(const lds_f32x4*)lds_at(base + 2 * TILE + (16 * (pp >> 1) + 4 * (pp & 1)) * 4);
   };
   int c_s = 0, c_t = qfirst;  // ring stage and query tile of the tile being finished
   auto step = [&](int st, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
-    wait_stage<NB, STAGES - 1>(min(STAGES - 3, nsteps - 2 - st));  // tile st+1 landed
+    wait_stage<4, STAGES - 1>(min(STAGES - 3, nsteps - 2 - st));  // tile st+1 landed
     __syncthreads();  // ... for every wave; the stage of tile st-1 is free
     if (st + STAGES - 1 < nsteps) issue();
     const int c_n = c_s + 1 == STAGES ? 0 : c_s + 1;  // stage of tile st+1
     const unsigned cst = lsm + (unsigned)(c_s * BUF);
     const unsigned nst = lsm + (unsigned)(c_n * BUF);
-    const unsigned ob = opaque(nst + op_lane(lane));    // operand reads of tile st+1
-    const unsigned tb = opaque(cst + tr_lane(lane));    // transposing reads of tile st
-    const unsigned lb = opaque(cst + 32u * half);       // (lse, D) pairs of tile st
+    const unsigned o0 = opaque(nst + sw_op_lane(lane, 0));  // operand reads of tile st+1,
+    const unsigned o1 = opaque(nst + sw_op_lane(lane, 1));  // even and odd k-steps
+    const unsigned t0 = opaque(cst + sw_tr_lane(lane, 0));  // transposing reads of tile st,
+    const unsigned t1 = opaque(cst + sw_tr_lane(lane, 1));  // rows +0 and +8
+    const unsigned lb = opaque(cst + 32u * half);           // (lse, D) pairs of tile st
     const int qt0 = c_t * BQ;
     c_s = c_n;  // the cursors move on to tile st+1
     if (++c_t == nqt) c_t = qfirst;
@@ -497,8 +488,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     bf16x8 qa[KPF], da[KPF];
 #pragma unroll
     for (int u = 0; u < KPF; ++u) {
-      qa[u] = op_read(ob, u);
-      da[u] = op_read(ob + 2 * TILE, u);
+      qa[u] = op_read((u & 1) ? o1 : o0, u);
+      da[u] = op_read(((u & 1) ? o1 : o0) + TILE, u);
     }
     f32x4 lp[PPK];
 #pragma unroll
@@ -512,8 +503,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int t = 0; t < DT; ++t) {
       bf16x8 qn = qa[t % KPF], dn = da[t % KPF];
       if (t + KPF < DT) {
-        qn = op_read(ob, t + KPF);
-        dn = op_read(ob + 2 * TILE, t + KPF);
+        qn = op_read(((t + KPF) & 1) ? o1 : o0, t + KPF);
+        dn = op_read((((t + KPF) & 1) ? o1 : o0) + TILE, t + KPF);
       }
       f32x4 ln[PPK];
 #pragma unroll
@@ -522,7 +513,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < TPK; ++i) {
           const int idx = (t - DT / 2) * TPK + i;
-          trop[idx] = tr_read(tb + ((idx & 1) ? TILE : 3 * TILE), idx >> 2, (idx >> 1) & 1);
+          const unsigned tt = (idx & 1) ? 0u : (unsigned)TILE;  // Q^T or dO^T
+          trop[idx] = sw_tr_read(t0 + tt, t1 + tt, idx >> 2, (idx >> 1) & 1);
         }
       }
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t % KPF], kreg[t], sn, 0, 0, 0);
@@ -547,7 +539,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     // the second half of the phase-2 operands
 #pragma unroll
     for (int idx = NTR / 2; idx < NTR; ++idx)
-      trop[idx] = tr_read(tb + ((idx & 1) ? TILE : 3 * TILE), idx >> 2, (idx >> 1) & 1);
+      trop[idx] = sw_tr_read(t0 + ((idx & 1) ? 0u : (unsigned)TILE), t1 + ((idx & 1) ? 0u : (unsigned)TILE),
+                             idx >> 2, (idx >> 1) & 1);
     // The asm MFMAs below read P and dS, just written by VALU: the hazard recognizer does
     // not see them, so five wait states are spelled out here, after the last write (the
     // operands are tied to this statement so that no write can move past it).
@@ -567,7 +560,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (st < nsteps) issue();
   f32x16 sA, dA, sB, dB;
   if (nsteps > 0) {
-    wait_stage<NB, STAGES>(min(STAGES - 2, nsteps - 1));  // tile 0 landed
+    wait_stage<4, STAGES>(min(STAGES - 2, nsteps - 1));  // tile 0 landed
     __syncthreads();
     products(sA, dA);
   }
