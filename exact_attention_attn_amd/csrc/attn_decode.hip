@@ -11,30 +11,33 @@
 //  * a wavefront reads 16-token chunks: 16 lanes x 16 bytes cover one token's
 //    d = 128 head row, 4 token rows per load instruction, whole 256-byte segments;
 //    the next two chunks are already in flight while one is reduced;
-//  * q.k is a per-lane 8-term FMA plus a 4-step DPP reduction inside each 16-lane row;
+//  * q.k is a per-lane 8-term packed bf16 dot product (four v_dot2_f32_bf16) plus a
+//    4-step DPP reduction inside each 16-lane row; P V pairs two tokens per packed dot;
 //  * every lane-row runs the online-softmax recurrence (section 2.2 of the same page)
 //    on its own tokens; the four rows are merged at the end with the same rescale;
 //  * grouped-query attention (section "GQA" of the same page): query head h reads KV
-//    head h / (H / H_kv) in place; the query heads sharing a KV head are adjacent
-//    wavefronts of one workgroup, so the repeated reads of a KV row hit in cache.
+//    head h / (H / H_kv) in place; a wavefront serves GW query heads of one KV head
+//    from each K/V row it loads, and further heads of the group run in adjacent
+//    wavefronts of the workgroup, so their reads of the same rows hit in cache.
 // The second kernel merges the splits of each (sequence, head): with M = max_c m_c,
 // O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, lse = (M + log2 L) ln 2, in split
 // order (deterministic).  This is the online-softmax rescale applied to partial
 // states ("L2.5 SOTA Kernel", yulong.wang, section 2.2).
 #include "attn_internal.h"
+#include "attn_tile.h"
 
 namespace attn {
 namespace {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float bf_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+// (lo, hi) rounded to bf16 (nearest even) and packed
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(unsigned, bf16x2{(__bf16)lo, (__bf16)hi});
+}
 
 // DPP helpers inside 16-lane rows.
 template <int CTRL>
@@ -96,14 +99,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const uint16_t* __restrict__ Vc = (const uint16_t*)p.v_cache;
   const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_pages;
 
-  // q slices of this lane, one per head; scores are scaled after the sum
-  float qf[GW][8];
+  // q slices of this lane, one per head, as packed bf16 pairs; scores are scaled after
+  // the sum
+  u32x4 qp[GW];
 #pragma unroll
-  for (int j = 0; j < GW; ++j) {
-    const u32x4 u = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h0 + j) * D + cl * 8);
-    qf[j][0] = bf_lo(u.x); qf[j][1] = bf_hi(u.x); qf[j][2] = bf_lo(u.y); qf[j][3] = bf_hi(u.y);
-    qf[j][4] = bf_lo(u.z); qf[j][5] = bf_hi(u.z); qf[j][6] = bf_lo(u.w); qf[j][7] = bf_hi(u.w);
-  }
+  for (int j = 0; j < GW; ++j)
+    qp[j] = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h0 + j) * D + cl * 8);
 
   auto load_chunk = [&](int u, C& c) {
     const int t0 = t_begin + 16 * u;  // multiple of 16, inside one page
@@ -134,8 +135,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   }
   const float c2 = p.scale_log2;
 
+  // q.k and the P V sums use packed bf16 dot products (v_dot2_f32_bf16, fp32
+  // accumulate): q.k straight from the K words; for P V the lane's tokens of two
+  // consecutive load instructions are paired, P rounded to bf16 (as for the matrix-core
+  // product of the prefill kernel) and the two tokens' V elements packed by byte
+  // permutes shared by all GW heads.
+  static_assert(NI % 2 == 0, "token pairs");
   auto consume = [&](int u, const C& c) {
     const int t0 = t_begin + 16 * u;
+    unsigned vpair[NI / 2][8];  // (token 2 i, token 2 i + 1) of element e, bf16 pairs
+#pragma unroll
+    for (int i = 0; i < NI / 2; ++i) {
+      const u32x4 x = c.v[2 * i], y = c.v[2 * i + 1];
+      const unsigned xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vpair[i][2 * w] = __builtin_amdgcn_perm(yw[w], xw[w], 0x05040100u);      // low halves
+        vpair[i][2 * w + 1] = __builtin_amdgcn_perm(yw[w], xw[w], 0x07060302u);  // high halves
+      }
+    }
 #pragma unroll
     for (int j = 0; j < GW; ++j) {
       float s[NI];
@@ -143,14 +161,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const u32x4 w = c.k[i];
-        float d = qf[j][0] * bf_lo(w.x);
-        d = __builtin_fmaf(qf[j][1], bf_hi(w.x), d);
-        d = __builtin_fmaf(qf[j][2], bf_lo(w.y), d);
-        d = __builtin_fmaf(qf[j][3], bf_hi(w.y), d);
-        d = __builtin_fmaf(qf[j][4], bf_lo(w.z), d);
-        d = __builtin_fmaf(qf[j][5], bf_hi(w.z), d);
-        d = __builtin_fmaf(qf[j][6], bf_lo(w.w), d);
-        d = __builtin_fmaf(qf[j][7], bf_hi(w.w), d);
+        float d = dot2(w.x, qp[j].x, 0.f);
+        d = dot2(w.y, qp[j].y, d);
+        d = dot2(w.z, qp[j].z, d);
+        d = dot2(w.w, qp[j].w, d);
         d = group_sum<LPT>(d);
         const bool ok = t0 + i * TPI + g < t_end;
         s[i] = ok ? d * c2 : kNegInf;
@@ -163,18 +177,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float pv = exp2_fast(s[i] - muse);
-        rs += pv;
-        const u32x4 w = c.v[i];
-        acc[j][0] = __builtin_fmaf(pv, bf_lo(w.x), acc[j][0]);
-        acc[j][1] = __builtin_fmaf(pv, bf_hi(w.x), acc[j][1]);
-        acc[j][2] = __builtin_fmaf(pv, bf_lo(w.y), acc[j][2]);
-        acc[j][3] = __builtin_fmaf(pv, bf_hi(w.y), acc[j][3]);
-        acc[j][4] = __builtin_fmaf(pv, bf_lo(w.z), acc[j][4]);
-        acc[j][5] = __builtin_fmaf(pv, bf_hi(w.z), acc[j][5]);
-        acc[j][6] = __builtin_fmaf(pv, bf_lo(w.w), acc[j][6]);
-        acc[j][7] = __builtin_fmaf(pv, bf_hi(w.w), acc[j][7]);
+      for (int i = 0; i < NI / 2; ++i) {
+        const float p0 = exp2_fast(s[2 * i] - muse), p1 = exp2_fast(s[2 * i + 1] - muse);
+        rs += p0 + p1;
+        const unsigned pp = pack_bf16(p0, p1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = dot2(pp, vpair[i][e], acc[j][e]);
       }
       l[j] = l[j] * alpha + rs;
       m2[j] = mnew;
@@ -225,6 +233,191 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   }
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
+
+// 16 bytes per lane from a per-lane global address into LDS at byte address `lds` +
+// 16 lane (global_load_lds; the wait states after the M0 write are spelled out, as the
+// hazard recognizer does not see inside the asm).
+__device__ __forceinline__ void dma16_at(const void* src, unsigned lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(src)
+               : "memory", "m0");
+}
+
+// Grouped-query decode on the matrix cores, for groups large enough that the per-head
+// VALU work of decode_split_kernel would dominate: one wavefront per (sequence, split,
+// KV head, block of up to 32 of the query heads that read it).  Those query heads are
+// the rows of the forward kernel's tile products (padded to 32): S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, so one K/V read serves every head of the
+// block, with no cross-lane reductions and a cost that does not grow with the group.
+// The split's tokens stream through LDS in tiles of 32, gathered from their pages
+// (global_load_lds with per-lane addresses: the pools may exceed a buffer resource's
+// reach), three tiles in flight per wavefront; each wavefront owns its LDS and runs
+// without barriers.  K tiles are row-major with the 16-byte chunk index XOR-swizzled by
+// the token, so that each lane quad loads 64 contiguous bytes of one token row and the
+// operand reads (one token per lane) hit distinct banks; V tiles use the forward
+// kernel's [32-column block][token][64 B] layout for the transposing reads.  The partial
+// (acc, m, l) per (sequence, head, split) has the same form as decode_split_kernel's,
+// so decode_combine_kernel merges either.
+template <int D>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int BN = 32;                // tokens per tile
+  constexpr int DT = D / 16, DB = D / 32;
+  constexpr int TILE = BN * D * 2;      // bytes of one K or V tile
+  constexpr int NBLK = TILE / 1024;     // 1 KiB blocks per K or V tile
+  constexpr int CPR = D / 8;            // 16-byte chunks per token row
+  constexpr int RPB = 64 / CPR;         // token rows per K block
+  constexpr int STAGES = 3;
+  constexpr int VBLK = BN * 64;         // bytes per 32-column block of the V tile
+  // per stage: K tile (swizzled row-major), V tile ([32-column block][token][64 B])
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
+
+  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+  const int G = p.H / p.H_kv;
+  const int gblocks = (G + 31) / 32;
+  const int hk = blockIdx.x / gblocks, gb = blockIdx.x - hk * gblocks;
+  const int split = blockIdx.y, b = blockIdx.z;
+  const int ctx = p.context_lens[b];
+  const int t_begin = split * p.split_len;
+  if (t_begin >= ctx) return;  // no barriers in this kernel
+  const int t_end = min(ctx, t_begin + p.split_len);
+  const int ntiles = (t_end - t_begin + BN - 1) / BN;
+  const int g = gb * 32 + col;  // query head (within the group) of this lane's column
+  const bool hv = g < G;
+  const int h = hk * G + g;
+
+  // B operand Q^T: lane's column is head h; k-step t covers columns 16 t + 8 half ...
+  bf16x8 qreg[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (hv) u = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h) * D + 16 * t + 8 * half);
+    qreg[t] = as_bf16x8(u);
+  }
+#pragma unroll
+  for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(qreg[t]));  // wait for Q here, once
+
+  // swizzle of token row r: chunk c sits at slot c ^ sw(r)
+  auto sw = [](int r) { return (r / (16 / CPR)) % CPR; };
+  // DMA.  K block i: token RPB i + lane / CPR, slot lane % CPR (chunk slot ^ sw).
+  // V block i: column block i / 2, token 16 (i % 2) + lane / 4, chunk 4 (i / 2) + lane % 4.
+  // Each 16-token group of the tile lies in one page.
+  const int64_t tok_bytes = (int64_t)p.H_kv * D * 2;
+  const int64_t page_bytes = (int64_t)p.page_size * tok_bytes;
+  const int gpp = p.page_size / 16;  // 16-token groups per page
+  const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_pages;
+  const uint8_t* const kpool = (const uint8_t*)p.k_cache + (int64_t)hk * D * 2;
+  const uint8_t* const vpool = (const uint8_t*)p.v_cache + (int64_t)hk * D * 2;
+  const unsigned lsm = (unsigned)(uintptr_t)(const lds_void*)smem;
+  auto group_row = [&](int gi) -> int64_t {  // byte offset of the first token row of group gi
+    const int pg = bt[gi / gpp];
+    return (int64_t)pg * page_bytes + (int64_t)((gi % gpp) * 16) * tok_bytes;
+  };
+  auto row_of = [&](int tok, int64_t r0, int64_t r1) { return (tok < 16 ? r0 : r1) + (int64_t)(tok & 15) * tok_bytes; };
+  auto issue = [&](int j) {
+    const int t0 = t_begin + j * BN;              // a multiple of 32
+    const int last = t_end - t0 - 1;              // last valid token of the tile (>= 0)
+    const int gi = t0 >> 4;
+    const int64_t r0 = group_row(gi);
+    const int64_t r1 = last >= 16 ? group_row(gi + 1) : r0;
+    const unsigned st = lsm + (unsigned)((j % STAGES) * 2 * TILE);
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      const int tok = RPB * i + lane / CPR;
+      const int chunk = (lane % CPR) ^ sw(tok);
+      dma16_at(kpool + row_of(min(tok, last), r0, r1) + 16 * chunk, st + 1024 * i);
+    }
+    const int64_t vrow0 = row_of(min(lane >> 2, last), r0, r1);
+    const int64_t vrow1 = row_of(min(16 + (lane >> 2), last), r0, r1);
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+      dma16_at(vpool + ((i & 1) ? vrow1 : vrow0) + 16 * (lane & 3) + 64 * (i >> 1), st + TILE + 1024 * i);
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m2 = kNegInf, l = 0.f;
+  const float c2 = p.scale_log2;
+  // K operand of k-step t: token col, chunk 2 t + half, at col * 2 D + ((2 t ^ ks) * 16)
+  const int ks = half ^ sw(col);
+  const unsigned krow = (unsigned)(col * D * 2);
+  const unsigned vread = (unsigned)((4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (j < ntiles) issue(j);
+  for (int j = 0; j < ntiles; ++j) {
+    // this tile's 2 NBLK loads have landed; up to STAGES - 2 younger tiles stay in flight
+    if (j + 1 < ntiles)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NBLK) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
+    const unsigned st = lsm + (unsigned)((j % STAGES) * 2 * TILE);
+    // S^T = K Q^T
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const bf16x8 a = as_bf16x8(*(const lds_u32x4*)lds_at(st + krow + (unsigned)(((2 * t) ^ ks) * 16)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t], s, 0, 0, 0);
+    }
+    // online softmax per column (query head), base 2; tokens past the end -> -inf
+    const int rem = t_end - (t_begin + j * BN);  // valid tokens in this tile
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tok = 8 * (v >> 2) + 4 * half + (v & 3);
+      if (tok >= rem) s[v] = kNegInf;
+      mx = fmaxf(mx, s[v]);
+    }
+    mx = fmaxf(mx, xor32(mx)) * c2;
+    const float mnew = fmaxf(m2, mx);  // finite: every tile holds a valid token
+    if (__builtin_amdgcn_ballot_w64(mnew > m2) != 0) {
+      const float alpha = exp2_fast(m2 - mnew);  // 0 on the first tile
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      m2 = mnew;
+    }
+    bf16x8 pb[2];
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float pv = exp2_fast(__builtin_fmaf(s[v], c2, -m2));
+      rs += pv;
+      pb[v >> 3][v & 7] = (__bf16)pv;
+    }
+    l += rs + xor32(rs);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 2; ++t4) {
+        const unsigned vp = st + TILE + vread + db * VBLK + t4 * 1024;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vp));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vp + 512));
+        const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t4], oacc[db], 0, 0, 0);
+      }
+  }
+
+  if (hv) {  // the partial state of head h: O^T column, (m, l)
+    const int64_t slot = ((int64_t)b * p.H + h) * p.max_splits + split;
+    float* dst = p.ws_acc + slot * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(float4*)(dst + 32 * db + 8 * i + 4 * half) =
+            make_float4(oacc[db][4 * i], oacc[db][4 * i + 1], oacc[db][4 * i + 2], oacc[db][4 * i + 3]);
+    if (half == 0) *(float2*)(p.ws_ml + slot * 2) = make_float2(m2, l);
+  }
+}
+
 // One wavefront per (sequence, head); lane owns D/64 columns.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams p) {
@@ -270,11 +463,18 @@ template <int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   if (p.B <= 0 || p.H <= 0) return hipSuccess;
   if (p.max_splits > 0) {
-    // query heads per wavefront: the largest of 4 (d = 64 only: register budget), 2, 1
-    // that divides the group size
     const int group = p.H / p.H_kv;
     hipError_t e;
-    if (D == 64 && group % 4 == 0)
+#ifndef ATTN_DECODE_MFMA_MIN_GROUP
+#define ATTN_DECODE_MFMA_MIN_GROUP 4
+#endif
+    if (group >= ATTN_DECODE_MFMA_MIN_GROUP) {  // larger groups: the matrix-core kernel
+      dim3 grid((unsigned)(p.H_kv * ((group + 31) / 32)), (unsigned)p.max_splits, (unsigned)p.B);
+      hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(64), 0, s, p);
+      e = hipGetLastError();
+    } else if (D == 64 && group % 4 == 0)  // query heads per wavefront of the VALU kernel:
+                                           // the largest of 4 (d = 64 only: register
+                                           // budget), 2, 1 that divides the group size
       e = launch_split<D, 4>(p, s);
     else if (group % 2 == 0)
       e = launch_split<D, 2>(p, s);

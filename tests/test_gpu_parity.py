@@ -343,10 +343,14 @@ def test_varlen_gqa(A, H, Hkv, d):
     assert_close("lse", host(lse), rl, TOL_BF16_LSE)
 
 
-@pytest.mark.parametrize("H,Hkv,d", [(16, 8, 128), (8, 1, 64), (32, 4, 128)])
-def test_decode_gqa(A, H, Hkv, d):
+@pytest.mark.parametrize("H,Hkv,d,page", [(16, 8, 128, 16), (8, 1, 64, 16), (32, 4, 128, 16), (6, 2, 128, 16),
+                                          (32, 1, 128, 16), (48, 1, 128, 16), (64, 1, 64, 16), (12, 3, 64, 48),
+                                          (16, 4, 128, 32)])
+def test_decode_gqa(A, H, Hkv, d, page):
+    """Groups of 2 .. 64 query heads per KV head (one and several blocks of 32 heads,
+    partial blocks, an odd group), d = 64 and 128, page sizes 16, 32 and 48."""
     import torch
-    w = synth.paged(H=H, d=d, seed=43, ctx=[1, 17, 600, 1024, 33, 512, 513, 2000], H_kv=Hkv)
+    w = synth.paged(H=H, d=d, seed=43, ctx=[1, 17, 600, 1024, 33, 512, 513, 2000], H_kv=Hkv, page=page)
     o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
                                  dev(w.context_lens), int(w.context_lens.max()), scale=w.scale)
     torch.cuda.synchronize()
