@@ -3,23 +3,23 @@
 // to FlashAttention and paged execution" (dlog.com.cn), sections 3.4 "Decode and the
 // KV cache" and "PagedAttention": one kernel covers the whole batch).
 //
-// The work is HBM-bound (about one flop per byte read), so the design is about
-// keeping many bytes in flight, not about matrix cores:
-//  * split-KV: each (sequence, split of kDecodeSplit tokens, head) is one wavefront,
-//    so a batch with a long-tailed length mix still yields thousands of equal-sized
-//    work units;
-//  * a wavefront reads 16-token chunks: 16 lanes x 16 bytes cover one token's
-//    d = 128 head row, 4 token rows per load instruction, whole 256-byte segments;
-//    the next two chunks are already in flight while one is reduced;
-//  * q.k is a per-lane 8-term packed bf16 dot product (four v_dot2_f32_bf16) plus a
-//    4-step DPP reduction inside each 16-lane row; P V pairs two tokens per packed dot;
-//  * every lane-row runs the online-softmax recurrence (section 2.2 of the same page)
-//    on its own tokens; the four rows are merged at the end with the same rescale;
-//  * grouped-query attention (section "GQA" of the same page): query head h reads KV
-//    head h / (H / H_kv) in place; a wavefront serves GW query heads of one KV head
-//    from each K/V row it loads, and further heads of the group run in adjacent
-//    wavefronts of the workgroup, so their reads of the same rows hit in cache.
-// The second kernel merges the splits of each (sequence, head): with M = max_c m_c,
+// The work is HBM-bound (about one flop per byte read per query head), so the design is
+// about keeping many bytes in flight:
+//  * split-KV: each (sequence, split of kDecodeSplit tokens, KV head or head) is one
+//    wavefront, so a batch with a long-tailed length mix still yields thousands of
+//    equal-sized work units;
+//  * one query head per KV head (decode_split_kernel, VALU): a wavefront reads 16-token
+//    chunks, 16 lanes x 16 bytes covering one token's d = 128 head row, 4 token rows per
+//    load instruction, the next two chunks in flight while one is reduced; q.k is a
+//    per-lane packed bf16 dot product (four v_dot2_f32_bf16) plus a 4-step DPP
+//    reduction inside each 16-lane row, P V pairs two tokens per packed dot; every
+//    lane-row runs the online-softmax recurrence (section 2.2 of the same page) on its
+//    own tokens and the four rows are merged at the end with the same rescale;
+//  * grouped-query attention (section "GQA" of the same page; query head h reads KV head
+//    h / (H / H_kv)): decode_mfma_kernel runs the query heads of one KV head as the rows
+//    of matrix-core tiles, so each K/V row is read once for the whole group and the
+//    per-head cost is absorbed by the MFMA.
+// The combine kernel merges the splits of each (sequence, head): with M = max_c m_c,
 // O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, lse = (M + log2 L) ln 2, in split
 // order (deterministic).  This is the online-softmax rescale applied to partial
 // states ("L2.5 SOTA Kernel", yulong.wang, section 2.2).
@@ -69,7 +69,8 @@ struct Chunk {
 };
 
 // One wavefront per (sequence, split, GW consecutive query heads).  The GW heads share
-// one KV head (GW divides H / H_kv), so each K/V row is loaded once for all of them.
+// one KV head (GW divides H / H_kv), so each K/V row is loaded once for all of them
+// (launched with GW = 1: grouped-query decode uses decode_mfma_kernel).
 template <int D, int GW>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
   using C = Chunk<D>;
@@ -236,44 +237,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
 
-// 16 bytes per lane from a per-lane global address into LDS at byte address `lds` +
-// 16 lane (global_load_lds; the wait states after the M0 write are spelled out, as the
-// hazard recognizer does not see inside the asm).
-__device__ __forceinline__ void dma16_at(const void* src, unsigned lds) {
-  const unsigned m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(src)
-               : "memory", "m0");
-}
-
-// Grouped-query decode on the matrix cores, for groups large enough that the per-head
-// VALU work of decode_split_kernel would dominate: one wavefront per (sequence, split,
+// Grouped-query decode on the matrix cores (the per-head VALU work of
+// decode_split_kernel grows with the group): one wavefront per (sequence, split,
 // KV head, block of up to 32 of the query heads that read it).  Those query heads are
 // the rows of the forward kernel's tile products (padded to 32): S^T = K Q^T and
 // O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, so one K/V read serves every head of the
 // block, with no cross-lane reductions and a cost that does not grow with the group.
-// The split's tokens stream through LDS in tiles of 32, gathered from their pages
-// (global_load_lds with per-lane addresses: the pools may exceed a buffer resource's
-// reach), three tiles in flight per wavefront; each wavefront owns its LDS and runs
-// without barriers.  K tiles are row-major with the 16-byte chunk index XOR-swizzled by
-// the token, so that each lane quad loads 64 contiguous bytes of one token row and the
-// operand reads (one token per lane) hit distinct banks; V tiles use the forward
-// kernel's [32-column block][token][64 B] layout for the transposing reads.  The partial
-// (acc, m, l) per (sequence, head, split) has the same form as decode_split_kernel's,
-// so decode_combine_kernel merges either.
+// Memory side, as in decode_split_kernel: 16-token halves of a tile (one page group
+// each) load into registers with whole-row coalesced loads, the next tile's two halves
+// in flight while a tile is computed;
+// each tile is then written to the wavefront's own LDS stage in the layouts the
+// products read (no barriers: a wavefront reads only what it wrote).  K: row-major with
+// the 16-byte chunk index XOR-swizzled by the token (conflict-free operand reads, one
+// token per lane).  V: chunk c of token r at c * 512 + (r ^ 4 (c % 4)) * 16, read by
+// ds_read_b64_tr_b16 as the V^T operand.  The partial (acc, m, l) per (sequence, head,
+// split) has the same form as decode_split_kernel's, so decode_combine_kernel merges
+// either.
 template <int D>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int BN = 32;                // tokens per tile
   constexpr int DT = D / 16, DB = D / 32;
   constexpr int TILE = BN * D * 2;      // bytes of one K or V tile
-  constexpr int NBLK = TILE / 1024;     // 1 KiB blocks per K or V tile
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  constexpr int RPB = 64 / CPR;         // token rows per K block
-  constexpr int STAGES = 3;
-  constexpr int VBLK = BN * 64;         // bytes per 32-column block of the V tile
-  // per stage: K tile (swizzled row-major), V tile ([32-column block][token][64 B])
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
+  constexpr int TPI = 64 / CPR;         // token rows per load instruction
+  constexpr int NI = 16 / TPI;          // load instructions per tensor per 16-token half
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE];  // K tile, V tile
 
   const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
   const int G = p.H / p.H_kv;
@@ -284,7 +272,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   const int t_begin = split * p.split_len;
   if (t_begin >= ctx) return;  // no barriers in this kernel
   const int t_end = min(ctx, t_begin + p.split_len);
-  const int ntiles = (t_end - t_begin + BN - 1) / BN;
+  const int nt = t_end - t_begin;            // tokens of this split
+  const int ntiles = (nt + BN - 1) / BN;
   const int g = gb * 32 + col;  // query head (within the group) of this lane's column
   const bool hv = g < G;
   const int h = hk * G + g;
@@ -297,44 +286,51 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     if (hv) u = *(const u32x4*)((const uint16_t*)p.q + ((int64_t)b * p.H + h) * D + 16 * t + 8 * half);
     qreg[t] = as_bf16x8(u);
   }
+  // wait for Q here, once: a wait left to the compiler would land in the tile loop as a
+  // vmcnt(0) that also drains the next tile's loads
 #pragma unroll
-  for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(qreg[t]));  // wait for Q here, once
+  for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(qreg[t]));
 
-  // swizzle of token row r: chunk c sits at slot c ^ sw(r)
+  // swizzle of K token row r: chunk c sits at slot c ^ sw(r)
   auto sw = [](int r) { return (r / (16 / CPR)) % CPR; };
-  // DMA.  K block i: token RPB i + lane / CPR, slot lane % CPR (chunk slot ^ sw).
-  // V block i: column block i / 2, token 16 (i % 2) + lane / 4, chunk 4 (i / 2) + lane % 4.
-  // Each 16-token group of the tile lies in one page.
-  const int64_t tok_bytes = (int64_t)p.H_kv * D * 2;
-  const int64_t page_bytes = (int64_t)p.page_size * tok_bytes;
-  const int gpp = p.page_size / 16;  // 16-token groups per page
+  const int lr = lane / CPR, lc = lane % CPR;  // token row within an instruction, chunk
+  const int64_t tok_stride = (int64_t)p.H_kv * D;  // elements
+  const int64_t page_stride = (int64_t)p.page_size * tok_stride;
+  const int gpp = p.page_size / 16;                // 16-token groups per page
   const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_pages;
-  const uint8_t* const kpool = (const uint8_t*)p.k_cache + (int64_t)hk * D * 2;
-  const uint8_t* const vpool = (const uint8_t*)p.v_cache + (int64_t)hk * D * 2;
-  const unsigned lsm = (unsigned)(uintptr_t)(const lds_void*)smem;
-  auto group_row = [&](int gi) -> int64_t {  // byte offset of the first token row of group gi
-    const int pg = bt[gi / gpp];
-    return (int64_t)pg * page_bytes + (int64_t)((gi % gpp) * 16) * tok_bytes;
-  };
-  auto row_of = [&](int tok, int64_t r0, int64_t r1) { return (tok < 16 ? r0 : r1) + (int64_t)(tok & 15) * tok_bytes; };
-  auto issue = [&](int j) {
-    const int t0 = t_begin + j * BN;              // a multiple of 32
-    const int last = t_end - t0 - 1;              // last valid token of the tile (>= 0)
-    const int gi = t0 >> 4;
-    const int64_t r0 = group_row(gi);
-    const int64_t r1 = last >= 16 ? group_row(gi + 1) : r0;
-    const unsigned st = lsm + (unsigned)((j % STAGES) * 2 * TILE);
+  const uint16_t* const Kc = (const uint16_t*)p.k_cache + (int64_t)hk * D + lc * 8;
+  const uint16_t* const Vc = (const uint16_t*)p.v_cache + (int64_t)hk * D + lc * 8;
+  // The pages of halves hf and hf + 1 (lanes 0 and 1 of one vector load, fetched a tile
+  // ahead of use so that the load loop's own wait covers it); indices past the split's
+  // last token group are clamped to it.
+  const int gi0 = t_begin >> 4, gi_last = (t_end - 1) >> 4;
+  auto fetch_pages = [&](int hf) { return bt[min(gi0 + hf + (lane & 1), gi_last) / gpp]; };
+  // half hf of the split (tokens 16 hf .. 16 hf + 15, in page `page`) into registers;
+  // tokens past the end read as zero (they are masked, and zero V rows keep 0 * V finite)
+  auto load_half = [&](int hf, int page, u32x4* kr, u32x4* vr) {
+    const int gi = gi0 + hf;
+    const int64_t base = (int64_t)page * page_stride + (int64_t)((gi % gpp) * 16) * tok_stride;
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      const int tok = RPB * i + lane / CPR;
-      const int chunk = (lane % CPR) ^ sw(tok);
-      dma16_at(kpool + row_of(min(tok, last), r0, r1) + 16 * chunk, st + 1024 * i);
+    for (int i = 0; i < NI; ++i) {
+      const int r = TPI * i + lr;
+      u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
+      if (16 * hf + r < nt) {
+        kz = *(const u32x4*)(Kc + base + (int64_t)r * tok_stride);
+        vz = *(const u32x4*)(Vc + base + (int64_t)r * tok_stride);
+      }
+      kr[i] = kz;
+      vr[i] = vz;
     }
-    const int64_t vrow0 = row_of(min(lane >> 2, last), r0, r1);
-    const int64_t vrow1 = row_of(min(16 + (lane >> 2), last), r0, r1);
+  };
+  const unsigned lsm = (unsigned)(uintptr_t)(const lds_void*)smem;
+  // registers of half hf (position ph = 0 / 1 in the tile) -> the LDS tile
+  auto store_half = [&](int ph, const u32x4* kr, const u32x4* vr) {
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i)
-      dma16_at(vpool + ((i & 1) ? vrow1 : vrow0) + 16 * (lane & 3) + 64 * (i >> 1), st + TILE + 1024 * i);
+    for (int i = 0; i < NI; ++i) {
+      const int r = 16 * ph + TPI * i + lr;  // token row in the tile
+      *(lds_u32x4*)lds_at(lsm + (unsigned)(r * D * 2 + ((lc ^ sw(r)) * 16))) = kr[i];
+      *(lds_u32x4*)lds_at(lsm + TILE + (unsigned)(lc * 512 + ((r ^ (4 * (lc & 3))) * 16))) = vr[i];
+    }
   };
 
   f32x16 oacc[DB];
@@ -344,29 +340,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
   const float c2 = p.scale_log2;
   // K operand of k-step t: token col, chunk 2 t + half, at col * 2 D + ((2 t ^ ks) * 16)
   const int ks = half ^ sw(col);
-  const unsigned krow = (unsigned)(col * D * 2);
-  const unsigned vread = (unsigned)((4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
+  const unsigned kread = lsm + (unsigned)(col * D * 2);
+  // V^T operand: 8 bytes of chunk 4 db + j of rows 16 t4 + x and 16 t4 + x + 8
+  const int vx = 4 * half + (lane & 15) / 4, vj = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const unsigned vlo = lsm + TILE + (unsigned)(vj * 512 + ((vx ^ (4 * vj)) * 16) + 8 * (lane & 1));
+  const unsigned vhi = lsm + TILE + (unsigned)(vj * 512 + (((vx ^ (4 * vj)) ^ 8) * 16) + 8 * (lane & 1));
 
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (j < ntiles) issue(j);
-  for (int j = 0; j < ntiles; ++j) {
-    // this tile's 2 NBLK loads have landed; up to STAGES - 2 younger tiles stay in flight
-    if (j + 1 < ntiles)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NBLK) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
-    const unsigned st = lsm + (unsigned)((j % STAGES) * 2 * TILE);
+  auto compute = [&](int j) {
     // S^T = K Q^T
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const bf16x8 a = as_bf16x8(*(const lds_u32x4*)lds_at(st + krow + (unsigned)(((2 * t) ^ ks) * 16)));
+      const bf16x8 a = as_bf16x8(*(const lds_u32x4*)lds_at(kread + (unsigned)(((2 * t) ^ ks) * 16)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[t], s, 0, 0, 0);
     }
     // online softmax per column (query head), base 2; tokens past the end -> -inf
-    const int rem = t_end - (t_begin + j * BN);  // valid tokens in this tile
+    const int rem = nt - j * BN;  // valid tokens in this tile
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -397,12 +386,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t4 = 0; t4 < 2; ++t4) {
-        const unsigned vp = st + TILE + vread + db * VBLK + t4 * 1024;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vp));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vp + 512));
+        const unsigned off = (unsigned)(db * 2048 + t4 * 256);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vlo + off));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)lds_at(vhi + off));
         const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t4], oacc[db], 0, 0, 0);
       }
+  };
+
+  // Two halves in registers: tile j's halves are written to LDS, then the next tile's
+  // halves load into the same registers while tile j is computed.
+  u32x4 kA[NI], vA[NI], kB[NI], vB[NI];
+  int pg = fetch_pages(0);
+  load_half(0, __builtin_amdgcn_readlane(pg, 0), kA, vA);
+  load_half(1, __builtin_amdgcn_readlane(pg, 1), kB, vB);
+  pg = fetch_pages(2);
+  for (int j = 0; j < ntiles; ++j) {
+    store_half(0, kA, vA);
+    store_half(1, kB, vB);
+    if (j + 1 < ntiles) {
+      load_half(2 * j + 2, __builtin_amdgcn_readlane(pg, 0), kA, vA);
+      load_half(2 * j + 3, __builtin_amdgcn_readlane(pg, 1), kB, vB);
+      pg = fetch_pages(2 * j + 4);
+    }
+    compute(j);
   }
 
   if (hv) {  // the partial state of head h: O^T column, (m, l)
@@ -463,23 +470,17 @@ template <int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   if (p.B <= 0 || p.H <= 0) return hipSuccess;
   if (p.max_splits > 0) {
+    // grouped-query attention: the matrix-core kernel (measured faster than the VALU
+    // kernel from two query heads per KV head on); one head per KV head: the VALU kernel
     const int group = p.H / p.H_kv;
     hipError_t e;
-#ifndef ATTN_DECODE_MFMA_MIN_GROUP
-#define ATTN_DECODE_MFMA_MIN_GROUP 4
-#endif
-    if (group >= ATTN_DECODE_MFMA_MIN_GROUP) {  // larger groups: the matrix-core kernel
+    if (group >= 2) {
       dim3 grid((unsigned)(p.H_kv * ((group + 31) / 32)), (unsigned)p.max_splits, (unsigned)p.B);
       hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(64), 0, s, p);
       e = hipGetLastError();
-    } else if (D == 64 && group % 4 == 0)  // query heads per wavefront of the VALU kernel:
-                                           // the largest of 4 (d = 64 only: register
-                                           // budget), 2, 1 that divides the group size
-      e = launch_split<D, 4>(p, s);
-    else if (group % 2 == 0)
-      e = launch_split<D, 2>(p, s);
-    else
+    } else {
       e = launch_split<D, 1>(p, s);
+    }
     if (e != hipSuccess) return e;
   }
   const int nbh = p.B * p.H;
