@@ -19,9 +19,10 @@
 //    the contraction follows the accumulator's layout, and V^T is read from LDS in
 //    that same order.  The O^T accumulator again gives each lane one query row, so
 //    the per-row rescale by exp(m_old - m_new) is a per-lane scalar multiply.
-//  * K and V tiles go global -> LDS with direct-to-LDS buffer loads (no VGPR staging),
-//    double-buffered; rows past the sequence end read as zero (buffer bounds) and are
-//    masked.  K tile: [key][16-byte chunk], chunk index XOR-swizzled by key so the
+//  * K and V tiles go global -> LDS with direct-to-LDS loads (no VGPR staging),
+//    double-buffered; rows past the sequence end are clamped to its last row and
+//    masked.  K tile: 1 KiB blocks of 16 keys x 64 B (one page group each, 64
+//    contiguous bytes per lane quad), the chunk order XOR-swizzled by key so that the
 //    MFMA operand reads hit distinct banks.  V tile: [32-column block][key][64 B]; the
 //    V^T operand comes from two LDS transposing reads (ds_read_b64_tr_b16), each
 //    covering 256 contiguous bytes.
@@ -37,6 +38,18 @@
 
 namespace attn {
 namespace {
+
+// 16 bytes per lane from a uniform base plus a 32-bit lane offset into LDS at `lds` +
+// 16 lane (global_load_lds with a scalar base: the paged gather, whose pools may exceed
+// a buffer resource's reach).  The wait states after the M0 write and after VALU writes
+// of the SGPR base are spelled out, as the hazard recognizer does not see inside the asm.
+__device__ __forceinline__ void dma16s(const void* sbase, int voff, const uint8_t* lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0v), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 
 // Block index -> (row block, batch/sequence, head).  Workgroups are dispatched
 // round-robin over the 8 XCDs (bid % 8), each with its own L2.  When the number of
@@ -124,9 +137,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
   static_assert(BPW * NW == NBLK, "tile split");
   // LDS: K and V tiles, each double-buffered.  K runs one tile ahead of V: while
   // tile j's V feeds P_j V_j, tile j+1's K feeds S_{j+1} = K_{j+1} Q^T.
-  //   K tile: in MFMA operand order, [DT k-steps][NS key blocks][2 halves][32 keys][16 B]:
-  //           the A operand of k-step t, key block c is the 1 KiB at (t * NS + c) * 1024,
-  //           lane i's 16 bytes at lane offset 16 i (no address arithmetic, no conflicts)
+  //   K tile: [BN / 16 key groups][NQ = D / 32 chunk quads] blocks of 1 KiB, each 16
+  //           keys x 64 B with the chunk within the quad XOR-swizzled by key bits 2-3:
+  //           chunk c of key k at ((k / 16) NQ + c / 4) 1024 + (k % 16) 64 +
+  //           ((c % 4) ^ ((k / 4) % 4)) 16.  A load block is one 16-key group (one page
+  //           of a paged pool) and each lane quad reads 64 contiguous bytes; the A operand
+  //           reads (one key per lane) hit distinct banks from two lane bases.
   //   V tile: [DB blocks][BN keys][4 chunks]  (32 columns of one key = 64 B)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];  // K0 K1 V0 V1
   uint8_t* const kbuf0 = smem;
@@ -181,10 +197,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int bi = wave * BPW + i;
-    {  // K block bi = (k-step t, key block c): key 32c + lane % 32, chunk 2t + lane / 32
-      const int t = bi / NS, c = bi % NS;
-      kkey[i] = 32 * c + (lane & 31);
-      kcol[i] = (2 * t + (lane >> 5)) * 16;
+    {  // K block bi = (key group g, chunk quad q): key 16 g + lane / 4, chunk
+       // 4 q + ((lane % 4) ^ ((lane / 16) % 4))
+      constexpr int NQ = D / 32;
+      const int g = bi / NQ, q = bi % NQ;
+      kkey[i] = 16 * g + (lane >> 2);
+      kcol[i] = (4 * q + ((lane & 3) ^ ((lane >> 4) & 3))) * 16;
     }
     {  // V block bi: column block bi / (BN / 16), keys 16 * (bi % (BN / 16)) + lane / 4, chunk lane % 4
       const int db = bi / (BN / 16);
@@ -195,33 +213,65 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
     vdoff[i] = vkey[i] * vrow_bytes + vcol[i];
   }
 
-  // Paged K/V: the physical page of each lane's key in the K (V) tile about to be loaded,
-  // fetched from the block table one step before its load is issued.
+  // Paged K/V: every 1 KiB load block covers one 16-key group of its tile, and a group
+  // lies in one page (page sizes are powers of two >= 16), so a block's source is a
+  // uniform base (its group's page, read from the block table one step before the load)
+  // plus a loop-invariant lane offset.  In the last tile, keys past the end are clamped
+  // to the last key, whose group then serves the whole block.
   const int32_t* __restrict__ bt_row = PAGED ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
   const int pshift = PAGED ? p.page_shift : 0;
   const int pmask = (1 << pshift) - 1;
-  int kpg[PAGED ? BPW : 1], vpg[PAGED ? BPW : 1];
-  auto load_pages = [&](int j, const int* key, int* pg) {
-    const int kt0 = j * BN;
-    const int last = Lk - kt0 - 1;
+  int kgrp[BPW], vgrp[BPW], kloff[BPW], vloff[BPW];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) pg[i] = bt_row[(kt0 + min(key[i], last)) >> pshift];
+  for (int i = 0; i < BPW; ++i) {
+    const int bi = wave * BPW + i;
+    kgrp[i] = bi / (D / 32);
+    vgrp[i] = bi % (BN / 16);
+    kloff[i] = (kkey[i] & 15) * krow_bytes + kcol[i];
+    vloff[i] = (vkey[i] & 15) * vrow_bytes + vcol[i];
+  }
+  // Page of block i's group.  A wavefront's K blocks are the NQ chunk quads of one key
+  // group, so K needs one page per tile (entry 0); V blocks span the tile's groups.
+  static_assert(BPW == D / 32, "a wavefront's K blocks share one key group");
+  int kpg[1], vpg[PAGED ? BPW : 1];
+  auto load_pages = [&](int j, const int* grp, int* pg, int n) {
+    const int kt0 = j * BN;
+    const int glast = (Lk - 1 - kt0) >> 4;  // last group holding a valid key
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+      if (i < n) pg[i] = bt_row[(kt0 + 16 * min(grp[i], glast)) >> pshift];
   };
-  auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* key, const int* colb,
-                         const int* pg, int row_bytes) {
+  // The page-id loads are ordinary loads that the compiler tracks, while the tile loads
+  // are asm it cannot see: once the tiles' own wait has covered the page ids, they pass
+  // through an empty asm so that no compiler wait for them lands between tile loads
+  // (where it would also wait for the tiles just issued).
+  auto settle_pages = [&]() {
+    asm volatile("" : "+v"(kpg[0]));
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) asm volatile("" : "+v"(vpg[i]));
+  };
+  auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* grp, const int* loff,
+                         const int* key, const int* colb, const int* pg, bool one_page, int row_bytes) {
     const int kt0 = j * BN;
     const int last = Lk - kt0 - 1;
+    const int glast = last >> 4;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int tok = kt0 + min(key[i], last);
-      const int64_t slot = ((int64_t)pg[i] << pshift) + (tok & pmask);
-      dma16g((const uint8_t*)base + slot * row_bytes + colb[i], buf + (wave * BPW + i) * 1024);
+      const int geff = min(grp[i], glast);
+      // the page id was loaded (one per lane, all equal) a step earlier and has landed with
+      // that step's tiles; it is moved to a scalar register only here, so that the
+      // compiler's wait for it does not also wait for the tiles just issued
+      const int page = __builtin_amdgcn_readfirstlane(pg[one_page ? 0 : i]);
+      const uint8_t* gbase =
+          (const uint8_t*)base + (((int64_t)page << pshift) + ((kt0 + 16 * geff) & pmask)) * row_bytes;
+      const int vo = last >= BN - 1 ? loff[i] : (min(key[i], last) - 16 * geff) * row_bytes + colb[i];
+      dma16s(gbase, vo, buf + (wave * BPW + i) * 1024);
     }
   };
 
   auto issue_k = [&](int j, uint8_t* kb) {
     if (PAGED) {
-      issue_paged(j, kb, Kg, kkey, kcol, kpg, krow_bytes);
+      issue_paged(j, kb, Kg, kgrp, kloff, kkey, kcol, kpg, true, krow_bytes);
       return;
     }
     const int kt0 = j * BN;
@@ -239,7 +289,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
   };
   auto issue_v = [&](int j, uint8_t* vb) {
     if (PAGED) {
-      issue_paged(j, vb, Vg, vkey, vcol, vpg, vrow_bytes);
+      issue_paged(j, vb, Vg, vgrp, vloff, vkey, vcol, vpg, false, vrow_bytes);
       return;
     }
     const int kt0 = j * BN;
@@ -264,12 +314,20 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
   const float c2 = p.scale_log2;
 
   // LDS read offsets
-  const int kread = lane * 16;
+  // K operand of k-step t, key block c: lane l reads chunk 2 t + l / 32 of key 32 c + l % 32,
+  // at kread[t % 2] + (2 c NQ + t / 2) 1024
+  constexpr int NQ = D / 32;
+  int kread[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int m = (lane >> 2) & 3;
+    kread[par] = ((lane >> 4) & 1) * NQ * 1024 + (lane & 15) * 64 + (2 * (par ^ (m >> 1)) + (half ^ (m & 1))) * 16;
+  }
   const int vread = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   // K operand of S^T = K Q^T for k-step t and key block c (16 bytes per lane)
   auto kop = [&](const uint8_t* kb, int t, int c) -> u32x4 {
-    return *(const lds_u32x4*)(kb + kread + (t * NS + c) * 1024);
+    return *(const lds_u32x4*)(kb + kread[t & 1] + (2 * c * NQ + (t >> 1)) * 1024);
   };
   // V^T operand of O^T += V^T P^T for column block db and key group t4 (two transposing reads)
   auto vop = [&](const uint8_t* vb, int db, int t4) -> bf16x8 {
@@ -293,18 +351,24 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
   if (ntiles > 0) {
     // prologue: K0, V0, K1 in flight; S_0 and its row max
     if (PAGED) {
-      load_pages(0, kkey, kpg);
-      load_pages(0, vkey, vpg);
+      load_pages(0, kgrp, kpg, 1);
+      load_pages(0, vgrp, vpg, BPW);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      settle_pages();
     }
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
     if (ntiles > 1) {
-      if (PAGED) load_pages(1, kkey, kpg);
+      if (PAGED) {
+        load_pages(1, kgrp, kpg, 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        settle_pages();
+      }
       issue_k(1, kbuf1);
     }
     if (PAGED) {  // pages of the first step's loads: K_2 and V_1
-      if (ntiles > 2) load_pages(2, kkey, kpg);
-      if (ntiles > 1) load_pages(1, vkey, vpg);
+      if (ntiles > 2) load_pages(2, kgrp, kpg, 1);
+      if (ntiles > 1) load_pages(1, vgrp, vpg, BPW);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -344,6 +408,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
                     f32x16* s_cur, f32x16* sn) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K_{j+1}, V_j landed
       __syncthreads();                                   // ... and every wave's
+      if (PAGED) settle_pages();  // the page ids loaded with them too
       // the first two k-steps' K operands are requested before anything else
       constexpr int KPF = 2;  // k-steps of K operands in flight
       u32x4 a[KPF][NS];
@@ -354,8 +419,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
       if (j + 2 < ntiles) issue_k(j + 2, kdma);
       if (j + 1 < ntiles) issue_v(j + 1, vdma);
       if (PAGED) {  // pages of the next step's loads, landing with this step's tiles
-        if (j + 3 < ntiles) load_pages(j + 3, kkey, kpg);
-        if (j + 2 < ntiles) load_pages(j + 2, vkey, vpg);
+        if (j + 3 < ntiles) load_pages(j + 3, kgrp, kpg, 1);
+        if (j + 2 < ntiles) load_pages(j + 2, vgrp, vpg, BPW);
       }
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {      // deferred rescale (rare)
         const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
