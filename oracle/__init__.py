@@ -9,7 +9,8 @@ Contents
 ``attention``      the plain definition softmax(scale * Q K^T) V, two-pass, fp64
 ``online``         the tiled online-softmax recurrence, used only to pin ``attention``
 
-``backward``       gradients dQ, dK, dV of the same definition (chain rule, fp64)
+``backward``       gradients dQ, dK, dV of the same definition (chain rule, fp64),
+                   dense and variable-length
 
 ``attention.store_kvcache`` is the plain scatter of new K/V rows into the page pools.
 
@@ -28,5 +29,5 @@ from .attention import (  # noqa: F401
     probabilities,
     store_kvcache,
 )
-from .backward import attention_backward_dense, attention_backward_rows  # noqa: F401
+from .backward import attention_backward_dense, attention_backward_rows, attention_backward_varlen  # noqa: F401
 from .online import online_attention  # noqa: F401

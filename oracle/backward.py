@@ -58,3 +58,27 @@ def attention_backward_dense(q, k, v, do, scale: float, causal: bool = False):
             dk[b, hk] += bk
             dv[b, hk] += bv
     return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, scale: float, causal: bool = False):
+    """Variable-length packed batch ("From standard Attention to FlashAttention and paged
+    execution", section 3.3: sequence s owns rows [cu_q[s], cu_q[s+1]) of Q, dO
+    [total_q, H, d] and [cu_k[s], cu_k[s+1]) of K, V [total_k, H_kv, d]; each sequence
+    attends independently, causal bottom-right aligned).  The gradient of the packed
+    batch is each sequence's gradient in its own rows; rows outside every sequence get
+    zero.  Returns dQ [total_q, H, d], dK, dV [total_k, H_kv, d] in float64."""
+    tq, H, d = q.shape
+    tk, H_kv = k.shape[0], k.shape[1]
+    dq = np.zeros((tq, H, d))
+    dk = np.zeros((tk, H_kv, d))
+    dv = np.zeros((tk, H_kv, v.shape[2]))
+    for s in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[s]), int(cu_q[s + 1])
+        k0, k1 = int(cu_k[s]), int(cu_k[s + 1])
+        for h in range(H):
+            hk = kv_head(h, H, H_kv)
+            a, bk, bv = attention_backward_rows(q[q0:q1, h], k[k0:k1, hk], v[k0:k1, hk], do[q0:q1, h], scale, causal)
+            dq[q0:q1, h] = a
+            dk[k0:k1, hk] += bk
+            dv[k0:k1, hk] += bv
+    return dq, dk, dv

@@ -581,3 +581,46 @@ def test_backward_optional_autograd_crosscheck():
     dq, dk, dv = oracle.attention_backward_rows(q, k, v, do, 0.5, True)
     for a, b in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
         assert np.abs(a - b.numpy()).max() < 1e-12
+
+
+def _varlen_loss(q, k, v, do, cu_q, cu_k, scale, causal):
+    o, _ = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    return float(np.nansum(o * do))
+
+
+def test_backward_varlen_matches_finite_differences():
+    """Central differences of <O, dO> through the varlen forward oracle, on a ragged
+    batch with grouped-query heads, Lq != Lk (bottom-right causal), an empty query
+    range and a trailing row outside every sequence (its gradient must be zero)."""
+    r = rng(78)
+    cu_q = np.array([0, 2, 2, 5])      # lengths 2, 0, 3; row 5 belongs to no sequence
+    cu_k = np.array([0, 3, 5, 7])      # lengths 3, 2, 2
+    H, H_kv, d = 2, 1, 2
+    q, do = r.normal(size=(6, H, d)), r.normal(size=(6, H, d))
+    k, v = r.normal(size=(7, H_kv, d)), r.normal(size=(7, H_kv, d))
+    dq, dk, dv = oracle.attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.8, True)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            up = _varlen_loss(q, k, v, do, cu_q, cu_k, 0.8, True)
+            x[idx] = x0 - eps
+            dn = _varlen_loss(q, k, v, do, cu_q, cu_k, 0.8, True)
+            x[idx] = x0
+            assert abs((up - dn) / (2 * eps) - g[idx]) < 1e-7, (idx, g[idx])
+    assert not dq[5].any()                   # outside every sequence
+    assert not dk[3:5].any() and not dv[3:5].any()  # keys of the sequence without queries
+
+
+def test_backward_varlen_one_sequence_is_dense():
+    """A one-sequence packed batch is the dense [1, H, N, d] case transposed."""
+    r = rng(79)
+    q, do = r.normal(size=(5, 4, 3)), r.normal(size=(5, 4, 3))
+    k, v = r.normal(size=(7, 2, 3)), r.normal(size=(7, 2, 3))
+    dq, dk, dv = oracle.attention_backward_varlen(q, k, v, do, np.array([0, 5]), np.array([0, 7]), 0.6, True)
+    t = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2))[None]
+    rq, rk, rv = oracle.attention_backward_dense(t(q), t(k), t(v), t(do), 0.6, True)
+    assert np.abs(dq - rq[0].transpose(1, 0, 2)).max() < TIGHT
+    assert np.abs(dk - rk[0].transpose(1, 0, 2)).max() < TIGHT
+    assert np.abs(dv - rv[0].transpose(1, 0, 2)).max() < TIGHT
