@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-One step = one call of each entry point on its workload, inputs resident in HBM:
+One step = one call of each entry point of the hot path on its workload, inputs
+resident in HBM:
   attn_fwd           B=1 H=32 N=8192 d=128 bf16 causal          (headline, TFLOP/s)
   attn_fwd_varlen    16 sequences, lengths U[128,4096], H=32 d=128 bf16 causal
   attn_decode_paged  64 sequences, context U[512,8192], 16-token pages, H=32 d=128 bf16
                      (headline, HBM GB/s)
+After the timed steps, the further entry points are timed the same way in a loop of
+their own (reported per entry point, not part of ms_per_step):
   attn_decode_paged  the same lengths with 16 query heads on 8 KV heads (grouped-query)
   attn_store_kvcache the varlen batch's 34069 new K/V rows written into 16-token pages
   attn_fwd_varlen    paged prefill: the second half of each of those sequences as new
                      causal rows over its whole context, read through the block table
   attn_bwd           dQ, dK, dV of the dense causal forward (by recomputation)
+  attn_bwd_varlen    dQ, dK, dV of the varlen forward
 
 W untimed warm-up steps, then K timed steps; every kernel call is bracketed by HIP
 events on the stream it runs on.  Prints ONE JSON line.  `value` is the dense
@@ -117,7 +121,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fwd", "varlen", "decode", "decode_gqa", "store_kvcache", "prefill_paged",
-                                       "bwd"],
+                                       "bwd", "bwd_varlen"],
                     default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +189,11 @@ def main() -> int:
     wsb = torch.empty(attn.attn_bwd_workspace_size(1, 32, 8192), dtype=torch.uint8, device="cuda")
     log(f"[bench] backward workload ready ({time.perf_counter() - t:.1f} s)")
 
+    do4 = dev(synth.normal(0, synth.T_DO, tuple(w4.q.shape), True))
+    dq4, dk4, dv4 = torch.empty_like(q4), torch.empty_like(k4), torch.empty_like(v4)
+    wsb4 = torch.empty(attn.attn_bwd_varlen_workspace_size(q4.shape[0], 32), dtype=torch.uint8, device="cuda")
+    log(f"[bench] varlen backward workload ready ({time.perf_counter() - t:.1f} s)")
+
     w7 = synth.workload("store_prefill")
     k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
     sl7 = torch.from_numpy(w7.slot_mapping).cuda()
@@ -208,38 +217,54 @@ def main() -> int:
     def run_bwd():
         attn.attn_bwd(q3, k3, v3, o3, l3, do3, scale=w3.scale, causal=True, dq=dq3, dk=dk3, dv=dv3, workspace=wsb)
 
+    def run_bwd_varlen():
+        attn.attn_bwd_varlen(q4, k4, v4, o4, l4, do4, cq4, ck4, w4.max_q, w4.max_k, scale=w4.scale, causal=True,
+                             dq=dq4, dk=dk4, dv=dv4, workspace=wsb4)
+
     def run_prefill_paged():
         attn.attn_fwd_varlen(q8, kc8, vc8, cq8, ck8, w8.max_q, w8.max_k, scale=w8.scale, causal=True,
                              out=o8, lse=l8, block_table=bt8)
 
-    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode), ("decode_gqa", run_decode_gqa),
-             ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged), ("bwd", run_bwd)]
+    # The timed step is the hot path proper: the dense forward, the varlen forward and
+    # paged decode.  The further entry points (grouped-query decode, store_kvcache, paged
+    # prefill, both backward passes) are timed after it, in a loop of their own of the
+    # same length, so that their heat does not lower the clock under the step's legs.
+    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode)]
+    extra = [("decode_gqa", run_decode_gqa), ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged),
+             ("bwd", run_bwd), ("bwd_varlen", run_bwd_varlen)]
     if args.only:
         parts = [p for p in parts if p[0] == args.only]
+        extra = [p for p in extra if p[0] == args.only]
 
-    for _ in range(args.warmup):
-        for _, fn in parts:
-            fn()
-    torch.cuda.synchronize()
+    def timed_loop(legs):
+        """W warm-up rounds, then K timed rounds of `legs`, each call bracketed by HIP
+        events on the current stream; returns the per-leg times and the loop's time."""
+        for _ in range(args.warmup):
+            for _, fn in legs:
+                fn()
+        torch.cuda.synchronize()
+        ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.steps)] for name, _ in legs}
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            for name, fn in legs:
+                a, b = ev[name][i]
+                a.record()
+                fn()
+                b.record()
+        end.record()
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        times = {name: np.array([a.elapsed_time(b) for a, b in ev[name]]) for name, _ in legs}
+        return times, start.elapsed_time(end), wall_s
 
-    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)] for name, _ in parts}
-    step_start = torch.cuda.Event(enable_timing=True)
-    step_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    step_start.record()
-    for i in range(args.steps):
-        for name, fn in parts:
-            a, b = ev[name][i]
-            a.record()
-            fn()
-            b.record()
-    step_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = step_start.elapsed_time(step_end)
-    ms = {name: np.array([a.elapsed_time(b) for a, b in ev[name]]) for name, _ in parts}
+    ms, ms_total, wall = timed_loop(parts) if parts else ({}, 0.0, 0.0)
+    if extra:
+        ms_extra, _, _ = timed_loop(extra)
+        ms.update(ms_extra)
     for name in ms:
         log(f"[bench] {name}: mean {ms[name].mean():.4f} ms  median {np.median(ms[name]):.4f}  min {ms[name].min():.4f}")
 
@@ -250,7 +275,7 @@ def main() -> int:
            "ms_per_step": ms_total / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "causal attention forward B=1 H=32 N=8192 d=128 bf16 (fp32 accumulate)",
-                      "step": [p[0] for p in parts], "device": dev_name}}
+                      "step": [p[0] for p in parts], "also_timed": [p[0] for p in extra], "device": dev_name}}
     if "fwd" in ms:
         t3 = ms["fwd"].mean() / 1e3
         ach = fl3 / t3 / 1e12
@@ -286,6 +311,12 @@ def main() -> int:
                       "ms": ms["bwd"].mean(), "tflops": flb / tb / 1e12, "frac": flb / tb / 1e12 / PEAK_BF16_TFLOPS,
                       "flops_per_launch": flb,
                       "note": "algorithmic flops 2.5x the forward's; the kernels recompute S and P twice"}
+    if "bwd_varlen" in ms:
+        tbv = ms["bwd_varlen"].mean() / 1e3
+        flv = varlen_flops(w4.lens_q, 32, 128)   # the varlen forward's
+        res["bwd_varlen"] = {"workload": "backward of the 16-sequence varlen forward (dQ, dK, dV)",
+                             "ms": ms["bwd_varlen"].mean(), "tflops": 2.5 * flv / tbv / 1e12,
+                             "frac": 2.5 * flv / tbv / 1e12 / PEAK_BF16_TFLOPS, "flops_per_launch": 2.5 * flv}
     if "prefill_paged" in ms:
         t8 = ms["prefill_paged"].mean() / 1e3
         lq8, lk8 = w8.lens_q.astype(np.float64), w8.lens_k.astype(np.float64)

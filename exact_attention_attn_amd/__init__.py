@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     AttnError,
     attn_bwd,
     attn_bwd_workspace_size,
+    attn_bwd_varlen,
+    attn_bwd_varlen_workspace_size,
     attn_decode_paged,
     attn_decode_paged_workspace_size,
     attn_fwd,

@@ -18,7 +18,8 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
-           "attn_store_kvcache", "attn_bwd", "attn_bwd_workspace_size", "attn_status_string", "attn_version")
+           "attn_store_kvcache", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_varlen",
+           "attn_bwd_varlen_workspace_size", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -54,6 +55,11 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_varlen_workspace_size.argtypes = [i32, i32]
+    lib.attn_bwd_varlen_workspace_size.restype = sz
+    lib.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    i32, i32, f32, i32, vp, sz, vp]
+    lib.attn_bwd_varlen.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -267,4 +273,47 @@ def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = F
                       B, H, Hkv, N, Nk, d, _dtype_code(q), scale, int(bool(causal)), _ptr(workspace),
                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen_workspace_size(total_q: int, H: int) -> int:
+    return int(load().attn_bwd_varlen_workspace_size(total_q, H))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None, workspace=None,
+                    stream=None):
+    """Gradients of attn_fwd_varlen.  q, o, dout [total_q, H, d]; k, v [total_k, H_kv, d]
+    (contiguous bf16); lse float32 [total_q, H] from the forward; cu_seqlens int32
+    [num_seqs + 1] on the device.  Returns (dq, dk, dv); rows outside every sequence are
+    left as they were in dq, dk, dv (zeros when they are allocated here)."""
+    torch = _torch()
+    lib = load()
+    Tq, H, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if k.shape != (Tk, Hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H_kv, d] matching q")
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (Tq, H):
+        raise ValueError("o and dout must match q, lse must be [total_q, H]")
+    for t in (q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k):
+        if not t.is_contiguous():
+            raise ValueError("backward tensors must be contiguous")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.zeros_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
+    need = attn_bwd_varlen_workspace_size(Tq, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+    rc = lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, Tq, Tk,
+                             int(max_seqlen_q), int(max_seqlen_k), H, Hkv, d, _dtype_code(q), scale, int(bool(causal)),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "attn_bwd_varlen")
     return dq, dk, dv

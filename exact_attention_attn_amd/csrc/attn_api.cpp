@@ -57,7 +57,7 @@ inline bool heads_ok(int H, int H_kv) { return H == 0 || (H_kv >= 1 && H_kv <= H
 
 extern "C" {
 
-int attn_version(void) { return 200; }
+int attn_version(void) { return 300; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -236,11 +236,58 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.ws = static_cast<float*>(workspace);
+  p.rows = (int64_t)B * H * N;
   p.B = B; p.H = H; p.H_kv = H_kv; p.N = N; p.Nk = Nk;
   p.kv_group = H / H_kv;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  return check_launch(attn::launch_bwd(p, d, causal != 0, reinterpret_cast<hipStream_t>(stream)));
+  return check_launch(attn::launch_bwd(p, d, causal != 0, false, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_varlen_workspace_size(int total_q, int H) {
+  if (total_q <= 0 || H <= 0) return 0;
+  return (size_t)total_q * H * 2 * sizeof(float);
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int num_seqs, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H, int H_kv,
+                    int d, int dtype, float scale, int causal, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || H < 0)
+    return fail(ATTN_ERR_INVALID_ARG);
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)num_seqs * H == 0 || (int64_t)max_seqlen_q + max_seqlen_k == 0) return ATTN_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID_ARG);
+  const bool rows = max_seqlen_q > 0, keys = max_seqlen_k > 0;
+  if (rows && (!q || !o || !dout || !lse || !dq)) return fail(ATTN_ERR_INVALID_ARG);
+  if (keys && (!k || !v || !dk || !dv)) return fail(ATTN_ERR_INVALID_ARG);
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  const size_t need = attn_bwd_varlen_workspace_size(total_q, H);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u)))
+    return fail(ATTN_ERR_INVALID_ARG);
+  // 32-bit byte offsets of one 32-row tile of token rows
+  if ((int64_t)32 * H * d * 2 > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED);
+
+  attn::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.ws = static_cast<float*>(workspace);
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.rows = (int64_t)total_q * H;
+  p.B = num_seqs; p.H = H; p.H_kv = H_kv; p.N = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.kv_group = H / H_kv;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  return check_launch(attn::launch_bwd(p, d, causal != 0, true, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -157,31 +157,32 @@ struct TilePairDma {
   static constexpr int TILE = 32 * D * 2, NB = TILE / 1024, NWU = NB / 2;
   static_assert(NB % 4 == 0, "whole groups of four blocks");
   int tsr;  // tensor of this wavefront's blocks
+  int rs;   // row stride of both tensors, elements
   int brow[4], bcol[4], voff[4];
-  __device__ void init(int wave, int lane) {
+  __device__ void init(int wave, int lane, int row_stride) {
+    rs = row_stride;
     tsr = min(1, 4 * wave / NB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = 2 * ((4 * wave + i) % NB) + (lane >> 5);
       brow[i] = (lane & 31) ^ (4 * (c & 3));
       bcol[i] = c * 16;
-      voff[i] = brow[i] * (D * 2) + bcol[i] - i * 1024 + kDmaBias;
+      voff[i] = brow[i] * (rs * 2) + bcol[i] - i * 1024 + kDmaBias;
     }
   }
-  // rows [r0, r0 + 32) of this wavefront's tensor (row-major, row stride D, `nrows`
-  // valid rows: later rows are clamped to the last one) into the stage at LDS byte
-  // address `stage`
+  // rows [r0, r0 + 32) of this wavefront's tensor (row stride rs, `nrows` valid rows:
+  // later rows are clamped to the last one) into the stage at LDS byte address `stage`
   __device__ void issue(const uint16_t* src, int r0, int nrows, unsigned stage, int wave) const {
     if (wave >= NWU) return;
     const int last = nrows - r0 - 1;  // >= 0
-    const u32x4s r = biased_rsrc(src + (int64_t)r0 * D);
+    const u32x4s r = biased_rsrc(src + (int64_t)r0 * rs);
     const unsigned m0 = stage + (unsigned)(wave * 4096);
     if (last >= 31) {
       dma4(r, m0, voff[0], voff[1], voff[2], voff[3]);
     } else {
       int vo[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vo[i] = min(brow[i], last) * (D * 2) + bcol[i] - i * 1024 + kDmaBias;
+      for (int i = 0; i < 4; ++i) vo[i] = min(brow[i], last) * (rs * 2) + bcol[i] - i * 1024 + kDmaBias;
       dma4(r, m0, vo[0], vo[1], vo[2], vo[3]);
     }
   }
@@ -205,6 +206,48 @@ __device__ __forceinline__ void wait_stage(int later) {
   wait_vm<0>();
 }
 
+// Extents and offsets of (sequence b, query head h, KV head hk).  Dense tensors are
+// [B, H, N, d] / [B, H_kv, Nk, d]; variable-length ones are token-major [total, H, d] /
+// [total, H_kv, d] with sequence b's rows from cu_q[b] / cu_k[b] (the forward's varlen
+// layout).  The lse and the workspace pairs follow the lse layout ([B, H, N] or
+// [total_q, H]); r0 / rrs index them.
+template <int D, bool VARLEN>
+struct BwdGeo {
+  int Lq, Lk;
+  int64_t q0, k0;  // element offsets of query row 0 of head h, key 0 of KV head hk
+  int qrs, krs;    // row strides, elements
+  int64_t qhs;     // element stride between consecutive query heads
+  int64_t r0;      // lse / workspace index of query row 0 of head h
+  int rrs;         // ... its stride between rows
+  int64_t rhs;     // ... and between consecutive query heads
+  __device__ BwdGeo(const BwdParams& p, int b, int h, int hk) {
+    if (VARLEN) {
+      const int qs = p.cu_q[b], ks = p.cu_k[b];
+      Lq = p.cu_q[b + 1] - qs;
+      Lk = p.cu_k[b + 1] - ks;
+      q0 = ((int64_t)qs * p.H + h) * D;
+      k0 = ((int64_t)ks * p.H_kv + hk) * D;
+      qrs = p.H * D;
+      krs = p.H_kv * D;
+      qhs = D;
+      r0 = (int64_t)qs * p.H + h;
+      rrs = p.H;
+      rhs = 1;
+    } else {
+      Lq = p.N;
+      Lk = p.Nk;
+      q0 = ((int64_t)b * p.H + h) * Lq * D;
+      k0 = ((int64_t)b * p.H_kv + hk) * Lk * D;
+      qrs = D;
+      krs = D;
+      qhs = (int64_t)Lq * D;
+      r0 = ((int64_t)b * p.H + h) * Lq;
+      rrs = 1;
+      rhs = Lq;
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------
 // (lse log2 e, D = dO . O) per query row
 // ------------------------------------------------------------------------------------
@@ -212,7 +255,7 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
   constexpr int LPR = D / 8;            // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;        // rows per workgroup
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const int64_t rows = p.rows;  // B H N, or total_q H (varlen): o, dO rows of D elements
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
   float s = 0.f;
@@ -234,7 +277,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const BwdParams p) {
 // ------------------------------------------------------------------------------------
 // dQ: 4 wavefronts x 32 query rows of one (b, h); key tiles of 32
 // ------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(const BwdParams p) {
   constexpr int NW = 4, BM = 32 * NW, BN = 32;
   constexpr int DT = D / 16, DB = D / 32;
@@ -247,16 +290,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int npairs = p.B * p.H;
   const int pair = blockIdx.x % npairs, rbi = blockIdx.x / npairs;
-  const int n_rb = (p.N + BM - 1) / BM;
+  const int n_rb = (p.N + BM - 1) / BM;  // p.N: the longest sequence's rows (varlen)
   const int rb = CAUSAL ? n_rb - 1 - rbi : rbi;  // heaviest row block first
   const int b = pair / p.H, h = pair - b * p.H, hk = h / p.kv_group;
-  const int Lq = p.N, Lk = p.Nk, shift = Lk - Lq;
+  const BwdGeo<D, VARLEN> geo(p, b, h, hk);
+  const int Lq = geo.Lq, Lk = geo.Lk, shift = Lk - Lq;
   const int row0 = rb * BM;
+  if (row0 >= Lq) return;  // uniform over the workgroup; no barrier passed yet
   const int qi = row0 + wave * 32 + (lane & 31);
-  const uint16_t* Q = (const uint16_t*)p.q + ((int64_t)b * p.H + h) * Lq * D;
-  const uint16_t* dO = (const uint16_t*)p.dout + ((int64_t)b * p.H + h) * Lq * D;
-  const uint16_t* K = (const uint16_t*)p.k + ((int64_t)b * p.H_kv + hk) * Lk * D;
-  const uint16_t* V = (const uint16_t*)p.v + ((int64_t)b * p.H_kv + hk) * Lk * D;
+  const uint16_t* Q = (const uint16_t*)p.q + geo.q0;
+  const uint16_t* dO = (const uint16_t*)p.dout + geo.q0;
+  const uint16_t* K = (const uint16_t*)p.k + geo.k0;
+  const uint16_t* V = (const uint16_t*)p.v + geo.k0;
 
   int kend = Lk;
   if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
@@ -269,15 +314,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int t = 0; t < DT; ++t) {
     u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
     if (qi < Lq) {
-      a = *(const u32x4*)(Q + (int64_t)qi * D + 16 * t + 8 * half);
-      c = *(const u32x4*)(dO + (int64_t)qi * D + 16 * t + 8 * half);
+      a = *(const u32x4*)(Q + (int64_t)qi * geo.qrs + 16 * t + 8 * half);
+      c = *(const u32x4*)(dO + (int64_t)qi * geo.qrs + 16 * t + 8 * half);
     }
     qreg[t] = as_bf16x8(a);
     dreg[t] = as_bf16x8(c);
   }
   float lse2 = 0.f, dsum = 0.f;
   if (qi < Lq) {
-    const float2 ld = *(const float2*)(p.ws + 2 * (((int64_t)b * p.H + h) * Lq + qi));
+    const float2 ld = *(const float2*)(p.ws + 2 * (geo.r0 + (int64_t)qi * geo.rrs));
     lse2 = ld.x;
     dsum = ld.y;
   }
@@ -288,7 +333,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const unsigned lsm = lds_addr(smem);
   TilePairDma<D> dma;
-  dma.init(wave, lane);
+  dma.init(wave, lane, geo.krs);
   const uint16_t* const src = dma.tsr ? V : K;
   auto issue = [&](int j) { dma.issue(src, j * BN, Lk, lsm + (unsigned)((j % STAGES) * 2 * TILE), wave); };
 
@@ -356,14 +401,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int t4 = 0; t4 < 2; ++t4)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db][t4], dsb[t4], acc[db], 0, 0, 0);
   }
-  if (qi < Lq) store_rows<DB>((uint16_t*)p.dq + ((int64_t)b * p.H + h) * Lq * D + (int64_t)qi * D, acc, p.scale, half);
+  if (qi < Lq) store_rows<DB>((uint16_t*)p.dq + geo.q0 + (int64_t)qi * geo.qrs, acc, p.scale, half);
 }
 
 // ------------------------------------------------------------------------------------
 // dK, dV: 4 wavefronts x 32 keys of one (b, KV head); query tiles of 32 of every query
 // head of the group
 // ------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NW = 4, BK = 32 * NW, BQ = 32;
   constexpr int DT = D / 16, DB = D / 32;
@@ -379,20 +424,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int npairs = p.B * p.H_kv;
   const int pair = blockIdx.x % npairs, kb = blockIdx.x / npairs;  // low (heaviest) key blocks first
   const int b = pair / p.H_kv, hk = pair - b * p.H_kv;
-  const int Lq = p.N, Lk = p.Nk, shift = Lk - Lq;
-  const int k0 = kb * BK;
-  const int key = k0 + wave * 32 + (lane & 31);  // this lane's key (accumulator column)
   const int G = p.kv_group;
-  const uint16_t* K = (const uint16_t*)p.k + ((int64_t)b * p.H_kv + hk) * Lk * D;
-  const uint16_t* V = (const uint16_t*)p.v + ((int64_t)b * p.H_kv + hk) * Lk * D;
+  const BwdGeo<D, VARLEN> geo(p, b, hk * G, hk);  // query head: the group's first
+  const int Lq = geo.Lq, Lk = geo.Lk, shift = Lk - Lq;
+  const int k0 = kb * BK;
+  if (k0 >= Lk) return;  // uniform over the workgroup; no barrier passed yet
+  const int key = k0 + wave * 32 + (lane & 31);  // this lane's key (accumulator column)
+  const uint16_t* K = (const uint16_t*)p.k + geo.k0;
+  const uint16_t* V = (const uint16_t*)p.v + geo.k0;
 
   bf16x8 kreg[DT], vreg[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
     if (key < Lk) {
-      a = *(const u32x4*)(K + (int64_t)key * D + 16 * t + 8 * half);
-      c = *(const u32x4*)(V + (int64_t)key * D + 16 * t + 8 * half);
+      a = *(const u32x4*)(K + (int64_t)key * geo.krs + 16 * t + 8 * half);
+      c = *(const u32x4*)(V + (int64_t)key * geo.krs + 16 * t + 8 * half);
     }
     kreg[t] = as_bf16x8(a);
     vreg[t] = as_bf16x8(c);
@@ -411,19 +458,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // DMA: the Q and dO tiles through TilePairDma; wavefront 0 also brings the tile's 32
   // (lse log2 e, D) pairs
   TilePairDma<D> dma;
-  dma.init(wave, lane);
-  const uint16_t* const src0 = (const uint16_t*)(dma.tsr ? p.dout : p.q) + ((int64_t)b * p.H + hk * G) * Lq * D;
-  const float* const ws0 = p.ws + 2 * ((int64_t)b * p.H + hk * G) * Lq;
+  dma.init(wave, lane, geo.qrs);
+  const uint16_t* const src0 = (const uint16_t*)(dma.tsr ? p.dout : p.q) + geo.q0;
+  const float* const ws0 = p.ws + 2 * geo.r0;
   // cursors: the next tile to load (head of the group, query tile) and its ring stage
   int ld_h = 0, ld_t = qfirst, ld_s = 0;
   auto issue = [&]() {
     const int qt0 = ld_t * BQ;
     const int last = Lq - qt0 - 1;  // last valid row of the tile (>= 0)
-    dma.issue(src0 + (int64_t)ld_h * Lq * D, qt0, Lq, lsm + (unsigned)(ld_s * BUF), wave);
+    dma.issue(src0 + (int64_t)ld_h * geo.qhs, qt0, Lq, lsm + (unsigned)(ld_s * BUF), wave);
     if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i
-      const float* ws = ws0 + 2 * ((int64_t)ld_h * Lq + qt0);
-      const u32x4s pr = buffer_rsrc(ws, ((int64_t)last + 1) * 8);
-      const int pv = min(lane >> 1, last) * 8 + (lane & 1) * 4;
+      const float* ws = ws0 + 2 * ((int64_t)ld_h * geo.rhs + (int64_t)qt0 * geo.rrs);
+      const u32x4s pr = buffer_rsrc(ws, ((int64_t)last * geo.rrs + 1) * 8);
+      const int pv = min(lane >> 1, last) * geo.rrs * 8 + (lane & 1) * 4;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :
                    : "s"(lsm + (unsigned)(ld_s * BUF + 2 * TILE)), "v"(pv), "s"(pr)
@@ -573,38 +620,45 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (st < nsteps) step(st, sA, dA, sB, dB);
   agpr_settle();
   if (key < Lk) {
-    const int64_t row = ((int64_t)b * p.H_kv + hk) * Lk * D + (int64_t)key * D;
+    const int64_t row = geo.k0 + (int64_t)key * geo.krs;
     store_rows<DB>((uint16_t*)p.dk + row, dk, p.scale, half);
     store_rows<DB>((uint16_t*)p.dv + row, dv, 1.0f, half);
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
-  if (rows > 0) {
+  // p.N, p.Nk: rows and keys per sequence (dense) or of the longest sequence (varlen)
+  if (p.rows > 0) {
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((p.rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nq = (int64_t)((p.N + 127) / 128) * p.B * p.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nq), dim3(256), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (nq > 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nq), dim3(256), 0, s, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   const int64_t nk = (int64_t)((p.Nk + 127) / 128) * p.B * p.H_kv;
   if (nk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nk), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nk), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool varlen, hipStream_t s) {
+  if (varlen) return causal ? launch_bwd_t<D, true, true>(p, s) : launch_bwd_t<D, false, true>(p, s);
+  return causal ? launch_bwd_t<D, true, false>(p, s) : launch_bwd_t<D, false, false>(p, s);
+}
+
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s) {
-  if (d == 128) return causal ? launch_bwd_t<128, true>(p, s) : launch_bwd_t<128, false>(p, s);
-  return causal ? launch_bwd_t<64, true>(p, s) : launch_bwd_t<64, false>(p, s);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, hipStream_t s) {
+  return d == 128 ? launch_bwd_d<128>(p, causal, varlen, s) : launch_bwd_d<64>(p, causal, varlen, s);
 }
 
 }  // namespace attn

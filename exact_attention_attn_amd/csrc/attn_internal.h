@@ -74,17 +74,21 @@ struct StoreParams {
 
 // Parameters of one backward launch (contiguous bf16 tensors).
 struct BwdParams {
-  const void* q;      // [B, H, N, d]
-  const void* k;      // [B, H_kv, Nk, d]
+  const void* q;      // [B, H, N, d]; varlen: [total_q, H, d]
+  const void* k;      // [B, H_kv, Nk, d]; varlen: [total_k, H_kv, d]
   const void* v;
-  const void* o;      // [B, H, N, d]
-  const void* dout;   // [B, H, N, d]
-  const float* lse;   // [B, H, N] (natural log)
-  void* dq;           // [B, H, N, d]
-  void* dk;           // [B, H_kv, Nk, d]
+  const void* o;      // as q
+  const void* dout;   // as q
+  const float* lse;   // [B, H, N] (natural log); varlen: [total_q, H]
+  void* dq;           // as q
+  void* dk;           // as k
   void* dv;
-  float* ws;          // [B, H, N, 2]: (lse * log2 e, dO . O) per query row
-  int B, H, H_kv, N, Nk;
+  float* ws;          // (lse * log2 e, dO . O) per query row, in lse order
+  const int32_t* cu_q;  // varlen: [B + 1] row starts of the B sequences (else null)
+  const int32_t* cu_k;
+  int64_t rows;       // query rows x heads: B H N, or total_q H
+  int B, H, H_kv;
+  int N, Nk;          // rows / keys per sequence; varlen: of the longest sequence
   int kv_group;       // H / H_kv
   float scale;
   float scale_log2;
@@ -95,7 +99,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, 
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
 hipError_t launch_store_kvcache(const StoreParams& p, hipStream_t s);
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, hipStream_t s);
 
 // Wavefronts per workgroup of the bf16 forward kernel; each owns 32 query rows.
 #ifndef ATTN_FWD_NW

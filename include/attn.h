@@ -14,7 +14,8 @@
  *                       (sections 3.4 and "PagedAttention");
  *   attn_store_kvcache  the step's new K/V rows written into the page pools
  *                       through slot_mapping;
- *   attn_bwd            the gradients dQ, dK, dV of attn_fwd by recomputation.
+ *   attn_bwd            the gradients dQ, dK, dV of attn_fwd by recomputation;
+ *   attn_bwd_varlen     the same for attn_fwd_varlen's packed batches.
  *
  * Each computes, per query row i, O_i = sum_j softmax_j(scale * q_i . k_j) v_j over
  * the admissible keys j, and the row's logsumexp lse_i = ln sum_j exp(scale * q_i . k_j)
@@ -196,6 +197,40 @@ size_t attn_bwd_workspace_size(int B, int H, int N);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int Nk, int d, int dtype,
              float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_varlen_workspace_size — bytes of device workspace attn_bwd_varlen needs
+ * (0 if none): 8 bytes per query row and head.
+ */
+size_t attn_bwd_varlen_workspace_size(int total_q, int H);
+
+/*
+ * attn_bwd_varlen — gradients of variable-length attention by recomputation (bfloat16):
+ * attn_bwd's method (same passages) applied to attn_fwd_varlen's packed batches
+ * (dlog.com.cn page, section 3.3: sequence s owns rows [cu_seqlens_q[s],
+ * cu_seqlens_q[s+1]) of the query-side tensors and [cu_seqlens_k[s], cu_seqlens_k[s+1])
+ * of the key-side ones, and attends only to its own keys; causal bottom-right per
+ * sequence).
+ *
+ * q, o, dout, dq : [total_q, H, d] contiguous;  k, v, dk, dv : [total_k, H_kv, d]
+ *       contiguous (contiguous K/V only: the paged layout has no backward here);
+ * lse : float32 [total_q, H], attn_fwd_varlen's logsumexp for the same inputs;
+ * cu_seqlens_q, cu_seqlens_k : int32 [num_seqs + 1] on the device, non-decreasing,
+ *       starting at 0, ending at most total_q / total_k;
+ * max_seqlen_q, max_seqlen_k : upper bounds of the per-sequence lengths (they size the
+ *       grid); total_q, total_k : the row counts of the tensors.
+ * Rows of dq (dk, dv) outside every sequence are not written; every other gradient
+ * entry is written exactly once, without atomics (deterministic), including zeros for
+ * keys no query row attends.
+ * workspace : at least attn_bwd_varlen_workspace_size(total_q, H) bytes, 8-byte aligned.
+ * dtype : ATTN_DTYPE_BF16 only; d 64 or 128.  ATTN_ERR_UNSUPPORTED when 32 H d * 2
+ * exceeds 2^31 - 1 (a tile's byte offsets are 32-bit).
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int num_seqs, int total_q, int total_k,
+                    int max_seqlen_q, int max_seqlen_k, int H, int H_kv, int d, int dtype, float scale,
+                    int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

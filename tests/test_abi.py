@@ -212,3 +212,41 @@ def test_bwd_rejects_before_launch(kw, status):
 def test_bwd_workspace_size():
     assert attn.attn_bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 8
     assert attn.attn_bwd_workspace_size(0, 3, 5) == 0
+
+
+def bwd_varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cq=FAKE, ck=FAKE, S=3,
+             Tq=300, Tk=400, mq=200, mk=250, H=4, Hkv=2, d=128, dtype=attn.ATTN_DTYPE_BF16, scale=0.1, causal=1,
+             ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return attn.load().attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                       a["cq"], a["ck"], a["S"], a["Tq"], a["Tk"], a["mq"], a["mk"], a["H"], a["Hkv"],
+                                       a["d"], a["dtype"], a["scale"], a["causal"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(causal=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(cq=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ck=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dv=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(wsb=300 * 4 * 8 - 1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(mq=301), attn.ATTN_ERR_INVALID_ARG),          # longer than the tensor
+    (dict(mk=401), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k=FAKE_ODD), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(S=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(S=0), attn.ATTN_OK),
+    (dict(mq=0, mk=0), attn.ATTN_OK),
+])
+def test_bwd_varlen_rejects_before_launch(kw, status):
+    assert bwd_varlen(**kw) == status
+
+
+def test_bwd_varlen_workspace_size():
+    assert attn.attn_bwd_varlen_workspace_size(300, 4) == 300 * 4 * 8
+    assert attn.attn_bwd_varlen_workspace_size(0, 4) == 0
