@@ -47,7 +47,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
 # kernel source they were taken on (sha256 prefix of attn_fwd.hip followed by the
 # attn_tile.h it includes); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "40f80cd71fcea801", "fetch_kib": 105693.0, "write_kib": 66561.0,
+FWD_COUNTERS = {"source_sha256_16": "5e7f3d8da064eb31", "fetch_kib": 103558.0, "write_kib": 66563.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
