@@ -336,11 +336,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
     const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  // tail keys and (causal) keys above the diagonal -> -inf; element (c, v) of the tile
-  auto mask1 = [&](int kt0, float x, int c, int v) -> float {
-    const int key = kt0 + 32 * c + 8 * (v >> 2) + 4 * half + (v & 3);
-    const bool ok = key < Lk && (!CAUSAL || key <= qi + shift);
-    return ok ? x : kNegInf;
+  // Tail keys and (causal) keys above the diagonal -> -inf.  A key is admissible for
+  // this lane's query iff key <= klim; element (c, v) of the tile
+  // at kt0 holds key kt0 + 4 half + 32 c + 8 (v / 4) + v % 4, so the test is one compare
+  // of that compile-time offset with klim - kt0 - 4 half.
+  const int klim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;
+  auto mask1 = [&](int rel, float x, int c, int v) -> float {
+    return 32 * c + 8 * (v >> 2) + (v & 3) <= rel ? x : kNegInf;
   };
   auto finish_max = [&](float mx, float& mnew, bool& grow) {
     mx = fmaxf(mx, xor32(mx)) * c2;
@@ -388,7 +390,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
       for (int c = 0; c < NS; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          if (nfull < 1) sA[c][v] = mask1(0, sA[c][v], c, v);
+          if (nfull < 1) sA[c][v] = mask1(klim - 4 * half, sA[c][v], c, v);
           mx = fmaxf(mx, sA[c][v]);
         }
       finish_max(mx, mnew, grow);
@@ -463,12 +465,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
       constexpr int SPC = 16 * NS / NCH;    // tile j+1 scores handled per chunk
       const int kt1 = (j + 1) * BN;
       float mx = kNegInf;
-      bf16x8 va = vop(vcur, 0, 0);
+      // V^T operands are read two MFMAs ahead: the transposing LDS reads take longer
+      // than one MFMA, and a one-ahead read made every MFMA of this phase wait for them
+      constexpr int VPF = 2;
+      bf16x8 vq[VPF];
+#pragma unroll
+      for (int u = 0; u < VPF; ++u) vq[u] = vop(vcur, u / NP, u % NP);
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
         const int db = k / NP, t4 = k % NP;
-        bf16x8 vn = va;
-        if (k + 1 < NCH) vn = vop(vcur, (k + 1) / NP, (k + 1) % NP);
+        const bf16x8 va = vq[k % VPF];
+        if (k + VPF < NCH) vq[k % VPF] = vop(vcur, (k + VPF) / NP, (k + VPF) % NP);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t4], oacc[db], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < SPC; ++e) {
@@ -477,15 +484,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AT
           mx = fmaxf(mx, sn[c][v]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        va = vn;
       }
+      // a use of the row max here keeps its max3 chain between the MFMAs above; otherwise
+      // the compiler sinks it past them into the unmasked branch below
+      asm volatile("" : "+v"(mx));
       if (j + 1 >= nfull) {  // tile j+1 crosses the diagonal or the tail: mask, redo the max
         mx = kNegInf;
 #pragma unroll
         for (int c = 0; c < NS; ++c)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            sn[c][v] = mask1(kt1, sn[c][v], c, v);
+            sn[c][v] = mask1(klim - kt1 - 4 * half, sn[c][v], c, v);
             mx = fmaxf(mx, sn[c][v]);
           }
       }
