@@ -188,23 +188,10 @@ struct TilePairDma {
   }
 };
 
-// Tiles stream through a ring of STAGES LDS buffers, STAGES - 1 ahead of use.  Before
-// using a stage, a wavefront waits for its own L direct-to-LDS loads of that stage while
-// up to `later` (<= STAGES - 2) younger stages stay in flight: loads complete in issue
-// order, so vmcnt(later * L) suffices (a wavefront that issued more than L loads for a
-// stage waits a little longer than needed).
+// s_waitcnt vmcnt(N): at most N of this wavefront's loads still in flight (loads
+// complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-template <int L, int STAGES>
-__device__ __forceinline__ void wait_stage(int later) {
-  if constexpr (STAGES >= 4) {
-    if (later >= 2) { wait_vm<2 * L>(); return; }
-  }
-  if constexpr (STAGES >= 3) {
-    if (later >= 1) { wait_vm<L>(); return; }
-  }
-  wait_vm<0>();
-}
 
 // Extents and offsets of (sequence b, query head h, KV head hk).  Dense tensors are
 // [B, H, N, d] / [B, H_kv, Nk, d]; variable-length ones are token-major [total, H, d] /
@@ -282,7 +269,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NW = 4, BM = 32 * NW, BN = 32;
   constexpr int DT = D / 16, DB = D / 32;
   constexpr int TILE = BN * D * 2;          // bytes of one [32, D] bf16 tile
-  constexpr int STAGES = 2;  // deeper rings measured no faster
+  // two stages: tile j in use, tile j+1 loading (deeper rings, and tiles loaded in
+  // pairs with a barrier every second step, measured no faster)
+  constexpr int STAGES = 2;
   // per stage: the K tile and the V tile, swizzled (sw_op_lane)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
 
@@ -366,13 +355,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (j < ntiles) issue(j);
+  if (ntiles > 0) issue(0);
   for (int j = 0; j < ntiles; ++j) {
-    wait_stage<4, STAGES>(min(STAGES - 2, ntiles - 1 - j));  // this wave's share of tile j
+    wait_vm<0>();     // this wave's share of tile j landed
     __syncthreads();  // ... and every wave's; the stage of tile j-1 is free
-    if (j + STAGES - 1 < ntiles) issue(j + STAGES - 1);
+    if (j + 1 < ntiles) issue(j + 1);
     const unsigned sbase = lsm + (unsigned)((j % STAGES) * 2 * TILE);
     const unsigned o0 = opaque(sbase + sw_op_lane(lane, 0)), o1 = opaque(sbase + sw_op_lane(lane, 1));
     const unsigned t0 = opaque(sbase + sw_tr_lane(lane, 0)), t1 = opaque(sbase + sw_tr_lane(lane, 1));
@@ -441,7 +428,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // per stage: the Q tile, the dO tile (swizzled layout, see sw_op_lane), then the
   // tile's 32 (lse log2 e, D) pairs
   constexpr int BUF = 2 * TILE + 256;
-  constexpr int STAGES = 3;  // tiles st (phase 2), st+1 (phase 1) and st+2 (loading)
+  // Tiles load in pairs and the workgroup synchronises every second step: the barrier
+  // of an even step st publishes tiles st+1 and st+2 (phase 1 of steps st and st+1)
+  // and then the pair st+3, st+4 is issued into the stages of tiles st-2 and st-1,
+  // which every wave finished before reaching that barrier.  Five stages.
+  // (a barrier every third or fourth step, with rings of 7 or 9 stages, measured slower)
+  constexpr int STAGES = 5;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -556,10 +548,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     return *(const lds_f32x4*)lds_at(base + 2 * TILE + (16 * (pp >> 1) + 4 * (pp & 1)) * 4);
   };
   int c_s = 0, c_t = qfirst;  // ring stage and query tile of the tile being finished
-  auto step = [&](int st, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
-    wait_stage<4, STAGES - 1>(min(STAGES - 3, nsteps - 2 - st));  // tile st+1 landed
-    __syncthreads();  // ... for every wave; the stage of tile st-1 is free
-    if (st + STAGES - 1 < nsteps) issue();
+  auto step = [&](int st, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn, bool sync) {
+    if (sync) {       // st even
+      wait_vm<0>();   // this wave's share of tiles st+1 and st+2 landed
+      __syncthreads();  // ... and every wave's; tiles st-2 and st-1 are finished
+      if (st + 3 < nsteps) issue();
+      if (st + 4 < nsteps) issue();
+    }
     const int c_n = c_s + 1 == STAGES ? 0 : c_s + 1;  // stage of tile st+1
     const unsigned cst = lsm + (unsigned)(c_s * BUF);
     const unsigned nst = lsm + (unsigned)(c_n * BUF);
@@ -642,22 +637,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
   };
 
+  // tiles 0, 1 and 2 before the loop (the first step's barrier publishes 1 and 2 again)
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
+  for (int st = 0; st < 3; ++st)
     if (st < nsteps) issue();
   f32x16 sA, dA, sB, dB;
   if (nsteps > 0) {
-    wait_stage<4, STAGES>(min(STAGES - 2, nsteps - 1));  // tile 0 landed
+    wait_vm<0>();
     __syncthreads();
     products(sA, dA);
   }
-  // unrolled by two so that the two S / dP sets swap roles without copies
+  // unrolled by two so that the two S / dP sets swap roles without copies; the even
+  // step of each pair synchronises
   int st = 0;
   for (; st + 1 < nsteps; st += 2) {
-    step(st, sA, dA, sB, dB);
-    step(st + 1, sB, dB, sA, dA);
+    step(st, sA, dA, sB, dB, true);
+    step(st + 1, sB, dB, sA, dA, false);
   }
-  if (st < nsteps) step(st, sA, dA, sB, dB);
+  if (st < nsteps) step(st, sA, dA, sB, dB, true);
   agpr_settle();
   if (key < Lk) {
     const int64_t row = geo.k0 + (int64_t)key * geo.krs;
