@@ -106,15 +106,14 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, hipSt
 #define ATTN_FWD_NW 4
 #endif
 constexpr int kFwdNW = ATTN_FWD_NW;
-// Wavefronts per SIMD the bf16 forward kernel is compiled for (register budget).
-#ifndef ATTN_FWD_WPE
-#define ATTN_FWD_WPE 2
-#endif
-// Keys per K/V tile of the bf16 forward kernel (32 or 64).
-#ifndef ATTN_FWD_BN
-#define ATTN_FWD_BN 64
-#endif
-constexpr int kFwdBN = ATTN_FWD_BN;
+// Tile configurations of the bf16 forward kernel: keys per K/V tile and wavefronts per
+// SIMD (the register budget).  64-key tiles at 2 wavefronts per SIMD by default; causal
+// variable-length (and paged) launches whose longest sequence is at most kFwdShortLen use
+// 32-key tiles at 3 wavefronts per SIMD (less masked work on the many diagonal tiles of
+// short sequences, and a third wavefront to cover the per-tile latencies).
+constexpr int kFwdBN = 64, kFwdWPE = 2;
+constexpr int kFwdShortBN = 32, kFwdShortWPE = 3;
+constexpr int kFwdShortLen = 4096;
 // Row-block height of the bf16 forward kernel (query rows per workgroup).
 constexpr int kFwdBM = 32 * kFwdNW;
 // Row-block height of the fp32 forward kernel.

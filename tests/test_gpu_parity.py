@@ -247,19 +247,29 @@ def test_varlen_edges(A, lens, lens_k, causal, d):
     assert_close("lse", host(lse), rl, TOL_BF16_LSE)
 
 
-def test_varlen_equals_dense_per_sequence(A):
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_dense_per_sequence(A, causal):
+    # Each packed sequence against the dense entry on that sequence alone.  Non-causal
+    # launches use the same tile configuration in both entries: bit-exact.  Causal
+    # varlen batches of short sequences take 32-key tiles where the dense entry keeps
+    # 64-key ones (another summation order): both within the bf16 tolerance of each
+    # other, which still catches any row or key taken from a neighbouring sequence.
     import torch
-    w = synth.varlen(H=4, d=128, causal=True, seed=3, lens=[130, 257, 64])
+    w = synth.varlen(H=4, d=128, causal=causal, seed=3, lens=[130, 257, 64])
     o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
-                               scale=w.scale, causal=True)
+                               scale=w.scale, causal=causal)
     for s in range(3):
         a, b = int(w.cu_q[s]), int(w.cu_q[s + 1])
         qd = dev(np.ascontiguousarray(w.q[a:b].transpose(1, 0, 2))[None])
         kd = dev(np.ascontiguousarray(w.k[a:b].transpose(1, 0, 2))[None])
         vd = dev(np.ascontiguousarray(w.v[a:b].transpose(1, 0, 2))[None])
-        od, ld = A.attn_fwd(qd, kd, vd, scale=w.scale, causal=True)
+        od, ld = A.attn_fwd(qd, kd, vd, scale=w.scale, causal=causal)
         torch.cuda.synchronize()
-        assert torch.equal(od[0].transpose(0, 1), o[a:b]) and torch.equal(ld[0].transpose(0, 1), lse[a:b])
+        if not causal:
+            assert torch.equal(od[0].transpose(0, 1), o[a:b]) and torch.equal(ld[0].transpose(0, 1), lse[a:b])
+        else:
+            assert_close(f"O seq {s}", host(o[a:b]), host(od[0].transpose(0, 1)), TOL_BF16_O)
+            assert_close(f"lse seq {s}", host(lse[a:b]), host(ld[0].transpose(0, 1)), TOL_BF16_LSE)
 
 
 @pytest.mark.parametrize("ctx,page", [([1, 15, 16, 17, 0, 511, 512, 513, 1024, 1500], 16),
@@ -595,17 +605,20 @@ def test_backward_varlen(A, lens, lens_k, H, Hkv, d, causal):
 
 
 def test_backward_varlen_one_sequence_equals_dense(A):
-    """A one-sequence packed batch runs the same arithmetic as the dense entry on the
-    transposed tensors: the gradients are bit-identical."""
-    w, do, dq, dk, dv = _bwd_varlen_case(A, [333], [400], 4, 2, 128, True, seed=83)
+    """A one-sequence packed batch runs the same backward arithmetic as the dense entry on
+    the transposed tensors (given the same O and lse): the gradients are bit-identical."""
     import torch
-    t = lambda x: dev(np.ascontiguousarray(x.transpose(1, 0, 2))[None])
-    q, k, v = t(w.q), t(w.k), t(w.v)
-    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=True)
-    gq, gk, gv = A.attn_bwd(q, k, v, o, lse, t(do), scale=w.scale, causal=True)
+    w = synth.varlen(H=4, d=128, causal=True, seed=83, lens=[333], lens_k=[400], H_kv=2)
+    do = synth.normal(83, synth.T_DO, (333, 4, 128), True)
+    q, k, v, cq, ck = dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k)
+    o, lse = A.attn_fwd_varlen(q, k, v, cq, ck, w.max_q, w.max_k, scale=w.scale, causal=True)
+    dq, dk, dv = A.attn_bwd_varlen(q, k, v, o, lse, dev(do), cq, ck, w.max_q, w.max_k, scale=w.scale, causal=True)
+    t = lambda x: x.transpose(0, 1).contiguous()[None]  # [total, H, d] -> [1, H, N, d]
+    gq, gk, gv = A.attn_bwd(t(q), t(k), t(v), t(o), lse.transpose(0, 1).contiguous()[None], t(dev(do)),
+                            scale=w.scale, causal=True)
     torch.cuda.synchronize()
     for a, b in ((dq, gq), (dk, gk), (dv, gv)):
-        assert np.array_equal(a, host(b)[0].transpose(1, 0, 2))
+        assert torch.equal(a, b[0].transpose(0, 1))
 
 
 def test_backward_varlen_deterministic(A):
