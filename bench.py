@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # (KiB per dispatch), scaled by what the same counters read for a 512 MiB device copy
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
 # kernel source they were taken on (sha256 prefix of attn_fwd.hip followed by the
-# attn_tile.h it includes); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "5e7f3d8da064eb31", "fetch_kib": 103558.0, "write_kib": 66563.0,
+# attn_tile.h and attn_internal.h it includes); reported as null otherwise.
+FWD_COUNTERS = {"source_sha256_16": "305a2e52714865fc", "fetch_kib": 105977.0, "write_kib": 66614.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -82,7 +82,7 @@ def fwd_traffic_bytes():
     changed since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "attn_tile.h"):
+    for name in ("attn_fwd.hip", "attn_tile.h", "attn_internal.h"):
         with open(os.path.join(ROOT, "exact_attention_attn_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     h = h.hexdigest()[:16]
