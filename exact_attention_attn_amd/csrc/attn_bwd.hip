@@ -323,26 +323,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   int nfull = Lk / BN;  // tiles that need no mask for any row of this workgroup
   if (CAUSAL) nfull = min(nfull, max(0, (row0 + shift + 1) / BN));
 
+  // Rows past the end load the last row (no divergent branch around the loads) and are
+  // zeroed; their results are never stored.
+  const bool qin = qi < Lq;
+  const int64_t qrow = min(qi, Lq - 1);
   bf16x8 qreg[DT], dreg[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (qi < Lq) {
-      a = *(const u32x4*)(Q + (int64_t)qi * geo.qrs + 16 * t + 8 * half);
-      c = *(const u32x4*)(dO + (int64_t)qi * geo.qrs + 16 * t + 8 * half);
-    }
-    qreg[t] = as_bf16x8(a);
-    dreg[t] = as_bf16x8(c);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 a = *(const u32x4*)(Q + qrow * geo.qrs + 16 * t + 8 * half);
+    const u32x4 c = *(const u32x4*)(dO + qrow * geo.qrs + 16 * t + 8 * half);
+    qreg[t] = as_bf16x8(qin ? a : z);
+    dreg[t] = as_bf16x8(qin ? c : z);
   }
-  float lse2 = 0.f, dsum = 0.f;
-  if (qi < Lq) {
-    const float2 ld = *(const float2*)(p.ws + 2 * (geo.r0 + (int64_t)qi * geo.rrs));
-    lse2 = ld.x;
-    dsum = ld.y;
-  }
-  settle(qreg);
-  settle(dreg);
-  asm volatile("" : "+v"(lse2), "+v"(dsum));
+  const float2 ld = *(const float2*)(p.ws + 2 * (geo.r0 + qrow * geo.rrs));
+  float lse2 = qin ? ld.x : 0.f, dsum = qin ? ld.y : 0.f;
   const float c2 = p.scale_log2;
 
   const unsigned lsm = lds_addr(smem);
@@ -356,6 +351,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   if (ntiles > 0) issue(0);
+  // the register loads above are waited for here, after the first tile's loads are
+  // issued, so that the two memory latencies overlap
+  settle(qreg);
+  settle(dreg);
+  asm volatile("" : "+v"(lse2), "+v"(dsum));
   for (int j = 0; j < ntiles; ++j) {
     wait_vm<0>();     // this wave's share of tile j landed
     __syncthreads();  // ... and every wave's; the stage of tile j-1 is free
@@ -465,19 +465,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* K = (const uint16_t*)p.k + geo.k0;
   const uint16_t* V = (const uint16_t*)p.v + geo.k0;
 
+  // keys past the end load the last key (no divergent branch around the loads) and are
+  // zeroed; their dK / dV are never stored
+  const bool kin = key < Lk;
+  const int64_t krow = min(key, Lk - 1);
   bf16x8 kreg[DT], vreg[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (key < Lk) {
-      a = *(const u32x4*)(K + (int64_t)key * geo.krs + 16 * t + 8 * half);
-      c = *(const u32x4*)(V + (int64_t)key * geo.krs + 16 * t + 8 * half);
-    }
-    kreg[t] = as_bf16x8(a);
-    vreg[t] = as_bf16x8(c);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 a = *(const u32x4*)(K + krow * geo.krs + 16 * t + 8 * half);
+    const u32x4 c = *(const u32x4*)(V + krow * geo.krs + 16 * t + 8 * half);
+    kreg[t] = as_bf16x8(kin ? a : z);
+    vreg[t] = as_bf16x8(kin ? c : z);
   }
-  settle(kreg);
-  settle(vreg);
   const float c2 = p.scale_log2;
 
   // query tiles of one head that can see any key of this block
@@ -641,6 +641,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int st = 0; st < 3; ++st)
     if (st < nsteps) issue();
+  // the K / V register loads are waited for here, after the first tiles' loads are issued
+  settle(kreg);
+  settle(vreg);
   f32x16 sA, dA, sB, dB;
   if (nsteps > 0) {
     wait_vm<0>();
