@@ -173,9 +173,12 @@ struct TilePairDma {
   // rows [r0, r0 + 32) of this wavefront's tensor (row stride rs, `nrows` valid rows:
   // later rows are clamped to the last one) into the stage at LDS byte address `stage`
   __device__ void issue(const uint16_t* src, int r0, int nrows, unsigned stage, int wave) const {
+    issue_at(src + (int64_t)r0 * rs, nrows - r0 - 1, stage, wave);
+  }
+  // the same from the tile's first row `tile` with `last` = index of its last valid row
+  __device__ void issue_at(const uint16_t* tile, int last, unsigned stage, int wave) const {
     if (wave >= NWU) return;
-    const int last = nrows - r0 - 1;  // >= 0
-    const u32x4s r = biased_rsrc(src + (int64_t)r0 * rs);
+    const u32x4s r = biased_rsrc(tile);
     const unsigned m0 = stage + (unsigned)(wave * 4096);
     if (last >= 31) {
       dma4(r, m0, voff[0], voff[1], voff[2], voff[3]);
@@ -493,25 +496,37 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   dma.init(wave, lane, geo.qrs);
   const uint16_t* const src0 = (const uint16_t*)(dma.tsr ? p.dout : p.q) + geo.q0;
   const float* const ws0 = p.ws + 2 * geo.r0;
-  // cursors: the next tile to load (head of the group, query tile) and its ring stage
-  int ld_h = 0, ld_t = qfirst, ld_s = 0;
+  // Cursors of the next tile to load, advanced by increments (with one wavefront per
+  // SIMD, every scalar instruction here delays this wavefront's MFMAs): its first query
+  // row, its rows in this wavefront's tensor and in the (lse, D) pairs, its ring stage.
+  int ld_q0 = qfirst * BQ;
+  const uint16_t* ld_src = src0 + (int64_t)ld_q0 * geo.qrs;
+  const float* ld_ws = ws0 + 2 * (int64_t)ld_q0 * geo.rrs;
+  unsigned ld_lds = lsm;
+  const int64_t src_tile = (int64_t)BQ * geo.qrs, ws_tile = 2 * (int64_t)BQ * geo.rrs;
+  // from one past the last tile of a head to the first tile of the next
+  const int64_t src_head = geo.qhs - (int64_t)per_head * src_tile;
+  const int64_t ws_head = 2 * geo.rhs - (int64_t)per_head * ws_tile;
+  const int pv_full = (lane >> 1) * geo.rrs * 8 + (lane & 1) * 4;  // pair rows of a full tile
   auto issue = [&]() {
-    const int qt0 = ld_t * BQ;
-    const int last = Lq - qt0 - 1;  // last valid row of the tile (>= 0)
-    dma.issue(src0 + (int64_t)ld_h * geo.qhs, qt0, Lq, lsm + (unsigned)(ld_s * BUF), wave);
-    if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i
-      const float* ws = ws0 + 2 * ((int64_t)ld_h * geo.rhs + (int64_t)qt0 * geo.rrs);
-      const u32x4s pr = buffer_rsrc(ws, ((int64_t)last * geo.rrs + 1) * 8);
-      const int pv = min(lane >> 1, last) * geo.rrs * 8 + (lane & 1) * 4;
+    const int last = Lq - ld_q0 - 1;  // last valid row of the tile (>= 0)
+    dma.issue_at(ld_src, last, ld_lds, wave);
+    if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i; rows clamped
+      const u32x4s pr = buffer_rsrc(ld_ws, 0x7FFFFFFF);
+      const int pv = last >= 31 ? pv_full : min(lane >> 1, last) * geo.rrs * 8 + (lane & 1) * 4;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :
-                   : "s"(lsm + (unsigned)(ld_s * BUF + 2 * TILE)), "v"(pv), "s"(pr)
+                   : "s"(ld_lds + (unsigned)(2 * TILE)), "v"(pv), "s"(pr)
                    : "memory", "m0");
     }
-    ld_s = ld_s + 1 == STAGES ? 0 : ld_s + 1;
-    if (++ld_t == nqt) {
-      ld_t = qfirst;
-      ++ld_h;
+    ld_lds = ld_lds + (unsigned)BUF == lsm + (unsigned)(STAGES * BUF) ? lsm : ld_lds + (unsigned)BUF;
+    ld_q0 += BQ;
+    ld_src += src_tile;
+    ld_ws += ws_tile;
+    if (ld_q0 >= Lq) {  // next head of the group
+      ld_q0 = qfirst * BQ;
+      ld_src += src_head;
+      ld_ws += ws_head;
     }
   };
 
