@@ -347,7 +347,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   TilePairDma<D> dma;
   dma.init(wave, lane, geo.krs);
   const uint16_t* const src = dma.tsr ? V : K;
-  auto issue = [&](int j) { dma.issue(src, j * BN, Lk, lsm + (unsigned)((j % STAGES) * 2 * TILE), wave); };
+  // tile j's rows: a cursor advanced by one tile per load
+  const uint16_t* ld_src = src;
+  const int64_t src_tile = (int64_t)BN * geo.krs;
+  auto issue = [&](int j) {
+    dma.issue_at(ld_src, Lk - j * BN - 1, lsm + (unsigned)((j % STAGES) * 2 * TILE), wave);
+    ld_src += src_tile;
+  };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -490,7 +496,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int nsteps = G * per_head;
 
   const unsigned lsm = lds_addr(smem);
-  // DMA: the Q and dO tiles through TilePairDma; wavefront 0 also brings the tile's 32
+  // DMA: the Q and dO tiles through TilePairDma; one wavefront also brings the tile's 32
   // (lse log2 e, D) pairs
   TilePairDma<D> dma;
   dma.init(wave, lane, geo.qrs);
@@ -503,6 +509,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* ld_src = src0 + (int64_t)ld_q0 * geo.qrs;
   const float* ld_ws = ws0 + 2 * (int64_t)ld_q0 * geo.rrs;
   unsigned ld_lds = lsm;
+  int ld_n = 0;  // tiles issued
   const int64_t src_tile = (int64_t)BQ * geo.qrs, ws_tile = 2 * (int64_t)BQ * geo.rrs;
   // from one past the last tile of a head to the first tile of the next
   const int64_t src_head = geo.qhs - (int64_t)per_head * src_tile;
@@ -511,7 +518,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   auto issue = [&]() {
     const int last = Lq - ld_q0 - 1;  // last valid row of the tile (>= 0)
     dma.issue_at(ld_src, last, ld_lds, wave);
-    if (wave == 0) {  // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i; rows clamped
+    // 32 (lse2, D) pairs: 64 dwords, lane i -> dword i; rows clamped.  The wavefront that
+    // loads them rotates with the tile, so that no wavefront is always the last at the
+    // barrier (each waits for its own loads before it).
+    if (wave == (ld_n & 3)) {
       const u32x4s pr = buffer_rsrc(ld_ws, 0x7FFFFFFF);
       const int pv = last >= 31 ? pv_full : min(lane >> 1, last) * geo.rrs * 8 + (lane & 1) * 4;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
@@ -519,6 +529,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
                    : "s"(ld_lds + (unsigned)(2 * TILE)), "v"(pv), "s"(pr)
                    : "memory", "m0");
     }
+    ++ld_n;
     ld_lds = ld_lds + (unsigned)BUF == lsm + (unsigned)(STAGES * BUF) ? lsm : ld_lds + (unsigned)BUF;
     ld_q0 += BQ;
     ld_src += src_tile;
