@@ -27,6 +27,8 @@
 // direct-to-LDS loads into one swizzled layout per tensor that serves both the 16-byte
 // operand reads and the ds_read_b64_tr_b16 transposing reads without bank conflicts.
 #include "attn_internal.h"
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace attn {
@@ -573,6 +575,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   auto pair_read = [&](unsigned base, int pp) -> f32x4 {
     return *(const lds_f32x4*)lds_at(base + 2 * TILE + (16 * (pp >> 1) + 4 * (pp & 1)) * 4);
   };
+  const int kw_last = k0 + 32 * wave + 31;  // this wavefront's last key
   int c_s = 0, c_t = qfirst;  // ring stage and query tile of the tile being finished
   auto step = [&](int st, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn, bool sync) {
     if (sync) {       // st even
@@ -606,7 +609,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     bf16x8 pb[2], dsb[2];
     sn = f32x16{};
     dpn = f32x16{};
-    // phase 1: S, dP of tile st+1; P, dS of tile st
+    // phase 1: S, dP of tile st+1; P, dS of tile st.  Two copies: tiles whose 32 rows
+    // see all 32 keys of this wavefront skip the mask (three VALU ops per element, a
+    // third of this kernel's VALU work).  Only phase 1 is duplicated: the dK / dV
+    // accumulators, written by inline-asm MFMAs, must not be joined by copies after a
+    // branch (the hazard recognizer cannot see that those asm statements are MFMAs).
+    auto phase1 = [&](auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       bf16x8 qn = qa[t % KPF], dn = da[t % KPF];
@@ -632,7 +641,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         const int v = t * EPK + e;
         const f32x4 pr = lp[e >> 1];
         const float l2 = (v & 1) ? pr.z : pr.x, dd = (v & 1) ? pr.w : pr.y;
-        const bool ok = (unsigned)(d0 + acc_row(v, 0)) < span;
+        const bool ok = !MASKED || (unsigned)(d0 + acc_row(v, 0)) < span;
         const float x = ok ? __builtin_fmaf(sc[v], c2, -l2) : kNegInf;  // exp2(-inf) = 0
         const float pv = exp2_fast(x);
         pb[v >> 3][v & 7] = (__bf16)pv;
@@ -644,6 +653,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int i = 0; i < PPK; ++i) lp[i] = ln[i];
     }
+    };
+    if (qt0 + BQ <= Lq && kw_last < Lk && (!CAUSAL || qt0 >= kw_last - shift)) phase1(std::false_type{});
+    else phase1(std::true_type{});
     // the second half of the phase-2 operands
 #pragma unroll
     for (int idx = NTR / 2; idx < NTR; ++idx)
