@@ -404,18 +404,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int t4 = 0; t4 < 2; ++t4) kt[db][t4] = sw_tr_read(t0, t1, db, t4);
     __builtin_amdgcn_sched_barrier(0);
     // dS^T = P^T (dP^T - D); keys past the end or above the diagonal have P = 0
-    const int base = j * BN + 4 * half;
-    int lim = BN;  // element offsets <= lim are admissible
-    if (j >= nfull) {
-      lim = Lk - 1 - base;
-      if (CAUSAL) lim = min(lim, qi + shift - base);
-    }
     bf16x8 dsb[2];
+    if (j < nfull) {  // no row of the workgroup needs a mask in this tile
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int off = 8 * (v >> 2) + (v & 3);
-      const float pv = exp2_fast(off <= lim ? __builtin_fmaf(s[v], c2, -lse2) : kNegInf);  // exp2(-inf) = 0
-      dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dsum));
+      for (int v = 0; v < 16; ++v) {
+        const float pv = exp2_fast(__builtin_fmaf(s[v], c2, -lse2));
+        dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dsum));
+      }
+    } else {
+      const int base = j * BN + 4 * half;
+      int lim = Lk - 1 - base;  // element offsets <= lim are admissible
+      if (CAUSAL) lim = min(lim, qi + shift - base);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int off = 8 * (v >> 2) + (v & 3);
+        const float pv = exp2_fast(off <= lim ? __builtin_fmaf(s[v], c2, -lse2) : kNegInf);  // exp2(-inf) = 0
+        dsb[v >> 3][v & 7] = (__bf16)(pv * (dp[v] - dsum));
+      }
     }
     // dQ^T += K^T dS^T
 #pragma unroll
