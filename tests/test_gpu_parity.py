@@ -116,6 +116,23 @@ def test_c4_varlen_full_sampled(A):
     assert np.isfinite(o).all()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_long_causal_sampled(A, d):
+    """A causal varlen batch whose longest sequence exceeds 4096 rows: the 64-key tile
+    configuration of the varlen entry (shorter batches take 32-key tiles)."""
+    import torch
+    w = synth.varlen(H=2, d=d, causal=True, seed=90 + d, lens=[4100, 300, 5003], lens_k=[4100, 301, 5003])
+    o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
+                               scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    rng = np.random.default_rng(104)
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, True,
+                                     rows_per_seq=lambda s, L: _rows(L, rng, 24))
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
 def test_c5_decode_full(A):
     import torch
     w = synth.workload("c5")
@@ -479,6 +496,7 @@ def _run_prefill(A, w):
     ([50, 129], [1000, 129], 8, 2, 64, 256, True),
     ([40, 90], [300, 90], 4, 2, 128, 16, False),
     ([0, 12, 3], [16, 12, 0], 4, 2, 128, 16, True),                      # empty query / empty context
+    ([4200, 30], [4500, 30], 2, 1, 128, 16, True),                       # > 4096 rows: 64-key tiles
 ])
 def test_paged_prefill(A, lq, lk, H, Hkv, d, page, causal):
     w = synth.paged_prefill(lq, lk, H, d, page, causal, seed=60, H_kv=Hkv)
