@@ -9,7 +9,9 @@
 // wavefronts (section 2.3, the FA2 split).
 //
 // gfx950 mapping (bf16 kernel):
-//  * workgroup = NW wavefronts x 32 query rows; key tiles of 64.
+//  * workgroup = NW wavefronts x 32 query rows; key tiles of 64 at 2 wavefronts per
+//    SIMD, or of 32 at 3 wavefronts per SIMD for causal varlen / paged batches of short
+//    sequences (kFwdShortLen).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows read from LDS, B = Q held in
 //    VGPRs for the whole loop.  In the 32x32 accumulator each lane then owns ONE
 //    query (column) and 16 keys, so the row max / row sum are 15 in-lane ops plus a
