@@ -1,9 +1,11 @@
 /*
- * attn.h — C ABI of libattn.so: exact attention forward for AMD Instinct MI355X (gfx950).
+ * attn.h — C ABI of libattn.so: exact attention, forward and backward, for AMD Instinct
+ * MI355X (gfx950).
  *
- * Three attention entry points, one per way the attention library is called on the
+ * Three forward entry points, one per way the attention library is called on the
  * dlog.com.cn page "From standard Attention to FlashAttention and paged execution",
- * and the KV-cache write that precedes them (attn_store_kvcache):
+ * the KV-cache write that precedes them (attn_store_kvcache), and the backward of the
+ * first two:
  *
  *   attn_fwd            fixed-length batched attention (section 3.1, the basic
  *                       fixed-length interface), layout [B, H, N, d] by default;
