@@ -101,6 +101,15 @@ def test_c3_bf16_causal_full_sampled(A):
     assert np.isfinite(o).all() and np.isfinite(lse).all()
 
 
+def test_dense_long_sequence_sampled(A):
+    """The longest dense sequence tested: causal N = 65536 (1024 key tiles for the last
+    row block), sampled rows including the last ones."""
+    w = synth.dense(B=1, H=2, N=65536, d=128, causal=True, seed=95)
+    rng = np.random.default_rng(105)
+    o, lse = _dense_sampled(A, w, [(0, 0), (0, 1)], _rows(w.N, rng, 16))
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
 def test_c4_varlen_full_sampled(A):
     import torch
     w = synth.workload("c4")
@@ -301,6 +310,23 @@ def test_decode_edges(A, ctx, page, d):
     ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
     assert_close("O", host(o), ro, TOL_BF16_O)
     assert_close("lse", host(lse), rl, TOL_BF16_LSE)
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (8, 2)])
+def test_decode_long_context(A, H, H_kv):
+    """The longest contexts tested: 65536 and 40001 tokens, 128 splits of the longest
+    sequence merged by the combine (one query head per KV head, and grouped-query)."""
+    import torch
+    ctx = [65536, 40001]
+    w = synth.paged(H=H, d=128, ctx=ctx, page=16, seed=96, H_kv=H_kv)
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), max(ctx), scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
 def test_decode_identity_table_equals_dense_last_row(A):
