@@ -712,3 +712,32 @@ def test_backward_full_causal_8192(A):
         _assert_grad(f"dQ[h={h}]", dq[0, h], rq)
         _assert_grad(f"dK[h={h}]", dk[0, h], rk)
         _assert_grad(f"dV[h={h}]", dv[0, h], rv)
+
+
+def test_side_stream_matches_default_stream(A):
+    """Launches go to the stream the caller names (torch's current stream by default):
+    the same calls on a side stream (default priority), implicitly and explicitly, give
+    the default stream's bits."""
+    import torch
+    w = synth.dense(B=1, H=4, N=300, d=128, causal=True, seed=97)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    wp = synth.paged(H=4, d=128, ctx=[700, 33], page=16, seed=98)
+    pq, kc, vc, bt, cl = dev(wp.q), dev(wp.k_cache), dev(wp.v_cache), dev(wp.block_table), dev(wp.context_lens)
+    do = dev(synth.normal(97, synth.T_DO, (1, 4, 300, 128), True))
+
+    def run(stream=None):
+        o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=True, stream=stream)
+        od, ld = A.attn_decode_paged(pq, kc, vc, bt, cl, 700, scale=wp.scale, stream=stream)
+        g = A.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True, stream=stream)
+        return (o, lse, od, ld) + tuple(g)
+
+    ref = run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        implicit = run()
+    explicit = run(stream=s)
+    s.synchronize()
+    for a, b, c in zip(ref, implicit, explicit):
+        assert torch.equal(a, b) and torch.equal(a, c)
