@@ -128,8 +128,8 @@ def main() -> int:
                     help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is described in DESIGN.md but not implemented.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented.", file=sys.stderr)
         return 2
 
     import torch

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale, short workspace */
-  ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d, dtype, alignment, page size) */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (d, dtype, alignment, page size) */
   ATTN_ERR_LAUNCH = 3       /* the HIP runtime reported an error at launch */
 } attn_status;
 

@@ -8,7 +8,7 @@ because the page's worked example of section 2.1 omits it).  The per-row
 logsumexp is the statistic the tiled forward writes next to O ("L2.5 SOTA
 Kernel", yulong.wang, sections 2.1 and 2.3).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * causal mask: key j is admissible for query row i iff j <= i + (Lk - Lq)
   (bottom-right alignment; j <= i when Lq == Lk);

@@ -575,7 +575,10 @@ def test_prefill_paged_full_sampled(A):
 
 # ------------------------------------------------------------------ backward
 
-TOL_BWD_REL = 2e-2   # max-abs error over max |reference| per gradient tensor (DESIGN.md §5)
+# Gradient tolerance (none is stated for gradients): dQ, dK, dV are written in bf16
+# (relative rounding 2^-9) from fp32 sums whose terms use bf16 P, dS and O (2^-9 each),
+# so each source is about 2e-3 of the largest entries; the bound is ten times that.
+TOL_BWD_REL = 2e-2   # max-abs error over max |reference| per gradient tensor
 
 
 def _bwd_case(A, B, H, Hkv, N, Nk, d, causal, seed):
