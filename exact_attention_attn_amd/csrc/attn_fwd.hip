@@ -440,7 +440,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
       for (int c = 0; c < NS; ++c) sn[c] = f32x16{};
       bf16x8 pb[NP];
+      // Row sum of P_j: with 64-key tiles at 2 wavefronts per SIMD the fp32 P values stay
+      // in registers and are summed in phase 2, whose VALU share is light (phase 1 carries
+      // the exponentials; measured +1 %); the 3-wavefront configuration has no registers
+      // to spare and sums in phase 1.
+      constexpr bool DEFER_SUM = WPE == 2;
       float rs = 0.f;
+      float pvs[DEFER_SUM ? 16 * NS : 1];
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         u32x4 n[NS];
@@ -453,14 +459,15 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         for (int e = 0; e < EPC; ++e) {
           const int idx = t * EPC + e;  // 0..16*NS-1: key group idx/8, element idx%8
           const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
-          rs += pv;
+          if constexpr (DEFER_SUM) pvs[idx] = pv;
+          else rs += pv;
           pb[idx >> 3][idx & 7] = (__bf16)pv;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < NS; ++c) a[t % KPF][c] = n[c];
       }
-      l += rs + xor32(rs);
+      if constexpr (!DEFER_SUM) l += rs + xor32(rs);
 
       // phase 2
       constexpr int NCH = NP * DB;          // O^T MFMAs per tile
@@ -484,9 +491,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
           const int idx = k * SPC + e;
           const int c = idx >> 4, v = idx & 15;
           mx = fmaxf(mx, sn[c][v]);
+          if constexpr (DEFER_SUM) rs += pvs[idx];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (DEFER_SUM) l += rs + xor32(rs);
       // a use of the row max here keeps its max3 chain between the MFMAs above; otherwise
       // the compiler sinks it past them into the unmasked branch below
       asm volatile("" : "+v"(mx));
