@@ -436,7 +436,6 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
       const float muse = (m2 == kNegInf) ? 0.f : m2;  // no admissible key yet: p = 0
 
       // phase 1
-      constexpr int EPC = 16 * NS / DT;  // exponentials per k-step
 #pragma unroll
       for (int c = 0; c < NS; ++c) sn[c] = f32x16{};
       bf16x8 pb[NP];
@@ -445,6 +444,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
       // the exponentials; measured +1 %); the 3-wavefront configuration has no registers
       // to spare and sums in phase 1.
       constexpr bool DEFER_SUM = WPE == 2;
+      // In that configuration the last MV elements of P_j are also computed in phase 2:
+      // its MFMAs then run key-group-major, so the last group's P operand is first needed
+      // at chunk (NP - 1) DB, after those elements (measured +0.7 %).
+      constexpr int MV = DEFER_SUM ? ((NP - 1) * DB < 4 ? (NP - 1) * DB : 4) : 0;
+      constexpr int P1 = 16 * NS - MV;  // elements of P_j computed in phase 1
       float rs = 0.f;
       float pvs[DEFER_SUM ? 16 * NS : 1];
 #pragma unroll
@@ -455,9 +459,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int c = 0; c < NS; ++c)
           sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[t % KPF][c]), qreg[t], sn[c], 0, 0, 0);
+        const int e0 = (t * P1) / DT, e1 = ((t + 1) * P1) / DT;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int idx = t * EPC + e;  // 0..16*NS-1: key group idx/8, element idx%8
+        for (int idx = e0; idx < e1; ++idx) {  // key group idx / 8, element idx % 8
           const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
           if constexpr (DEFER_SUM) pvs[idx] = pv;
           else rs += pv;
@@ -478,13 +482,22 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
       // than one MFMA, and a one-ahead read made every MFMA of this phase wait for them
       constexpr int VPF = 2;
       bf16x8 vq[VPF];
+      // chunk k's (column block, key group): key-group-major when elements moved here
+      auto cdb = [](int k) { return MV ? k % DB : k / NP; };
+      auto ct4 = [](int k) { return MV ? k / DB : k % NP; };
 #pragma unroll
-      for (int u = 0; u < VPF; ++u) vq[u] = vop(vcur, u / NP, u % NP);
+      for (int u = 0; u < VPF; ++u) vq[u] = vop(vcur, cdb(u), ct4(u));
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
-        const int db = k / NP, t4 = k % NP;
+        const int db = cdb(k), t4 = ct4(k);
+        if (k < MV) {  // element P1 + k of P_j
+          const int idx = P1 + k;
+          const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
+          pvs[idx] = pv;
+          pb[idx >> 3][idx & 7] = (__bf16)pv;
+        }
         const bf16x8 va = vq[k % VPF];
-        if (k + VPF < NCH) vq[k % VPF] = vop(vcur, (k + VPF) / NP, (k + VPF) % NP);
+        if (k + VPF < NCH) vq[k % VPF] = vop(vcur, cdb(k + VPF), ct4(k + VPF));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t4], oacc[db], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < SPC; ++e) {
