@@ -47,7 +47,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1).  Valid only for the
 # kernel source they were taken on (sha256 prefix of attn_fwd.hip followed by the
 # attn_tile.h and attn_internal.h it includes); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "7ea27a776777e384", "fetch_kib": 105482.0, "write_kib": 66606.0,
+FWD_COUNTERS = {"source_sha256_16": "c64ca604c5a83c35", "fetch_kib": 106049.0, "write_kib": 66592.0,
                 "fetch_scale": 2.0, "write_scale": 1.0}
 
 

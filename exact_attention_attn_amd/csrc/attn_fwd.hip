@@ -236,21 +236,23 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
   // group, so K needs one page per tile (entry 0); V blocks span the tile's groups.
   static_assert(BPW <= D / 32 && (D / 32) % BPW == 0, "a wavefront's K blocks share one key group");
   int kpg[1], vpg[PAGED ? BPW : 1];
+  // The page ids are uniform per wavefront: read through the constant address space,
+  // they become scalar loads into SGPRs (no VGPRs: the 32-key, 3-wavefront configuration
+  // spilled with them in VGPRs) whose wait counter is not the one of the tile loads.
+  // They are issued a step ahead and pass through an empty asm right after the step's
+  // barrier, so that the compiler's wait for them lands there.
   auto load_pages = [&](int j, const int* grp, int* pg, int n) {
     const int kt0 = j * BN;
     const int glast = (Lk - 1 - kt0) >> 4;  // last group holding a valid key
 #pragma unroll
     for (int i = 0; i < BPW; ++i)
-      if (i < n) pg[i] = bt_row[(kt0 + 16 * min(grp[i], glast)) >> pshift];
+      if (i < n)
+        pg[i] = *(const __attribute__((address_space(4))) int32_t*)(bt_row + ((kt0 + 16 * min(grp[i], glast)) >> pshift));
   };
-  // The page-id loads are ordinary loads that the compiler tracks, while the tile loads
-  // are asm it cannot see: once the tiles' own wait has covered the page ids, they pass
-  // through an empty asm so that no compiler wait for them lands between tile loads
-  // (where it would also wait for the tiles just issued).
   auto settle_pages = [&]() {
-    asm volatile("" : "+v"(kpg[0]));
+    asm volatile("" : "+s"(kpg[0]));
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) asm volatile("" : "+v"(vpg[i]));
+    for (int i = 0; i < BPW; ++i) asm volatile("" : "+s"(vpg[i]));
   };
   auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* grp, const int* loff,
                          const int* key, const int* colb, const int* pg, bool one_page, int row_bytes) {
@@ -260,10 +262,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int geff = min(grp[i], glast);
-      // the page id was loaded (one per lane, all equal) a step earlier and has landed with
-      // that step's tiles; it is moved to a scalar register only here, so that the
-      // compiler's wait for it does not also wait for the tiles just issued
-      const int page = __builtin_amdgcn_readfirstlane(pg[one_page ? 0 : i]);
+      const int page = pg[one_page ? 0 : i];  // scalar, loaded a step earlier
       const uint8_t* gbase =
           (const uint8_t*)base + (((int64_t)page << pshift) + ((kt0 + 16 * geff) & pmask)) * row_bytes;
       const int vo = last >= BN - 1 ? loff[i] : (min(key[i], last) - 16 * geff) * row_bytes + colb[i];
