@@ -282,7 +282,7 @@ def main() -> int:
         res["value"] = ach
         res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / PEAK_BF16_TFLOPS, "traffic": fwd_traffic_bytes(),
-                           "kernel": "fwd_bf16_kernel<128,4,causal>", "flops_per_launch": fl3,
+                           "kernel": "fwd_bf16_kernel<128, 4, 64, 2, true, false, false>", "flops_per_launch": fl3,
                            "algorithmic_bytes_per_launch": fwd_bytes(1, 32, 8192, 128)}
     else:
         res["value"] = None
