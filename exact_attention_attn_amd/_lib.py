@@ -107,6 +107,36 @@ def _check(rc: int, where: str):
         raise AttnError(rc, where)
 
 
+def _on_device(where: str, device, **tensors):
+    """Every tensor argument must live in GPU memory on ``device``: the library takes
+    raw device pointers, and a host address handed to a kernel would fault."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{where}: {name} must be a GPU tensor on {device} (got {t.device})")
+
+
+def _check_out(where: str, name: str, t, shape, dtype, contiguous: bool = True):
+    """A caller-given output must have the shape, dtype (and contiguity) the kernels
+    write: they store every element of the expected shape."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{where}: {name} must be {dtype} {tuple(shape)} (got {t.dtype} {tuple(t.shape)})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{where}: {name} must be contiguous")
+
+
+def _check_workspace(where: str, ws, need: int):
+    if ws is None:
+        return
+    if not ws.is_contiguous():
+        raise ValueError(f"{where}: workspace must be contiguous")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"{where}: workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
+
+
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse=None,
              with_lse: bool = True, stream=None):
     """Dense attention.  q [B, H, N, d], k/v [B, H_kv, Nk, d] (bf16 or fp32, any strides
@@ -121,6 +151,9 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
         raise ValueError("k and v must be [B, H_kv, Nk, d] matching q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
+    _on_device("attn_fwd", q.device, q=q, k=k, v=v, out=out, lse=lse)
+    _check_out("attn_fwd", "out", out, (B, H, N, d), q.dtype, contiguous=False)
+    _check_out("attn_fwd", "lse", lse, (B, H, N), torch.float32)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device) if out is None else out
     if with_lse and lse is None:
@@ -163,6 +196,12 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     num_seqs = cu_seqlens_q.numel() - 1
     if cu_seqlens_k.numel() != num_seqs + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if not cu_seqlens_q.is_contiguous() or not cu_seqlens_k.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    _on_device("attn_fwd_varlen", q.device, q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+               block_table=block_table, out=out, lse=lse)
+    _check_out("attn_fwd_varlen", "out", out, (tq, H, d), q.dtype)
+    _check_out("attn_fwd_varlen", "lse", lse, (tq, H), torch.float32)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     if with_lse and lse is None:
@@ -197,8 +236,15 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
             raise ValueError("decode tensors must be contiguous")
     if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_table and context_lens must be int32")
+    _on_device("attn_decode_paged", q.device, q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+               context_lens=context_lens, workspace=workspace, out=out, lse=lse)
+    _check_out("attn_decode_paged", "out", out, (B, H, d), q.dtype)
+    _check_out("attn_decode_paged", "lse", lse, (B, H), torch.float32)
+    if context_lens.numel() != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("context_lens must be [B] and block_table [B, max_pages]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = attn_decode_paged_workspace_size(B, H, d, int(max_context_len), page)
+    _check_workspace("attn_decode_paged", workspace, need)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q) if out is None else out
@@ -235,6 +281,7 @@ def attn_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None):
         raise TypeError("slot_mapping must be int64 [T]")
     if k.dtype != k_cache.dtype or v.dtype != k.dtype or v_cache.dtype != k.dtype:
         raise TypeError("k, v and the pools must share a dtype")
+    _on_device("attn_store_kvcache", k.device, k=k, v=v, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
     rc = lib.attn_store_kvcache(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, d,
                                 k.stride(0), v.stride(0), num_pages, page, _dtype_code(k), _stream(stream))
     _check(rc, "attn_store_kvcache")
@@ -262,11 +309,17 @@ def attn_bwd(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = F
             raise ValueError("backward tensors must be contiguous")
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
+    _on_device("attn_bwd", q.device, q=q, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv,
+               workspace=workspace)
+    _check_out("attn_bwd", "dq", dq, q.shape, q.dtype)
+    _check_out("attn_bwd", "dk", dk, k.shape, k.dtype)
+    _check_out("attn_bwd", "dv", dv, v.shape, v.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     need = attn_bwd_workspace_size(B, H, N)
+    _check_workspace("attn_bwd", workspace, need)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
     rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -304,11 +357,17 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
         raise TypeError("cu_seqlens must be int32")
     if cu_seqlens_q.numel() != cu_seqlens_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _on_device("attn_bwd_varlen", q.device, q=q, k=k, v=v, o=o, lse=lse, dout=dout, cu_seqlens_q=cu_seqlens_q,
+               cu_seqlens_k=cu_seqlens_k, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    _check_out("attn_bwd_varlen", "dq", dq, q.shape, q.dtype)
+    _check_out("attn_bwd_varlen", "dk", dk, k.shape, k.dtype)
+    _check_out("attn_bwd_varlen", "dv", dv, v.shape, v.dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.zeros_like(q) if dq is None else dq
     dk = torch.zeros_like(k) if dk is None else dk
     dv = torch.zeros_like(v) if dv is None else dv
     need = attn_bwd_varlen_workspace_size(Tq, H)
+    _check_workspace("attn_bwd_varlen", workspace, need)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
     rc = lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),

@@ -39,11 +39,12 @@ inline bool strides_aligned(const int64_t s[3], int esize) {
   return true;
 }
 
-inline int check_launch(hipError_t e) {
+inline int check_launch(hipError_t e, hipStream_t stream) {
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH);
   if (getenv("ATTN_DEBUG") != nullptr) {
-    // test aid: surface asynchronous faults at the call that caused them
-    if (hipDeviceSynchronize() != hipSuccess || hipGetLastError() != hipSuccess) return fail(ATTN_ERR_LAUNCH);
+    // test aid: surface asynchronous faults at the call that caused them (only the
+    // caller's stream is waited for, as every launch of the call went there)
+    if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return fail(ATTN_ERR_LAUNCH);
   }
   return ATTN_OK;
 }
@@ -110,10 +111,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_DTYPE_BF16) {
     p.n_rb = (N + attn::kFwdBM - 1) / attn::kFwdBM;
-    return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, false, s));
+    return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, false, s), s);
   }
   p.n_rb = (N + attn::kFwdF32BM - 1) / attn::kFwdF32BM;
-  return check_launch(attn::launch_fwd_f32(p, d, causal != 0, s));
+  return check_launch(attn::launch_fwd_f32(p, d, causal != 0, s), s);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -157,7 +158,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   p.kv_group = H / H_kv;
   p.n_rb = (max_seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM;
   p.scale_log2 = scale * kLog2e;
-  return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, true, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_fwd_bf16(p, d, causal != 0, true, s), s);
 }
 
 size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len, int page_size) {
@@ -196,12 +198,14 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
   p.block_table = block_table; p.context_lens = context_lens;
   p.B = B; p.H = H; p.H_kv = H_kv; p.max_pages = max_pages_per_seq; p.page_size = page_size;
   p.split_len = attn::kDecodeSplit;
+  p.max_ctx = max_context_len;
   p.max_splits = max_context_len > 0 ? n_splits(max_context_len) : 0;
   const size_t slots = (size_t)B * H * p.max_splits;
   p.ws_acc = static_cast<float*>(workspace);
   p.ws_ml = p.ws_acc ? p.ws_acc + slots * d : nullptr;
   p.scale_log2 = scale * kLog2e;
-  return check_launch(attn::launch_decode_paged(p, d, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_decode_paged(p, d, s), s);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N) {
@@ -241,7 +245,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.kv_group = H / H_kv;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  return check_launch(attn::launch_bwd(p, d, causal != 0, false, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_bwd(p, d, causal != 0, false, s), s);
 }
 
 size_t attn_bwd_varlen_workspace_size(int total_q, int H) {
@@ -287,7 +292,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.kv_group = H / H_kv;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  return check_launch(attn::launch_bwd(p, d, causal != 0, true, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_bwd(p, d, causal != 0, true, s), s);
 }
 
 int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -314,7 +320,8 @@ int attn_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cach
   p.num_slots = (int64_t)num_pages * page_size;
   p.T = T;
   p.row_bytes = (int)row;
-  return check_launch(attn::launch_store_kvcache(p, reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_store_kvcache(p, s), s);
 }
 
 }  // extern "C"

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const int b = blockIdx.z;
   const int h0 = hw * GW;                // first query head of this wave
   if (h0 >= p.H) return;  // no barriers in this kernel: waves are independent
-  const int ctx = p.context_lens[b];
+  const int ctx = min(p.context_lens[b], p.max_ctx);  // a longer length is a caller error: truncated
   const int t_begin = split * p.split_len;
   if (t_begin >= ctx) return;
   const int t_end = min(ctx, t_begin + p.split_len);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int gblocks = (G + 31) / 32;
   const int hk = blockIdx.x / gblocks, gb = blockIdx.x - hk * gblocks;
   const int split = blockIdx.y, b = blockIdx.z;
-  const int ctx = p.context_lens[b];
+  const int ctx = min(p.context_lens[b], p.max_ctx);  // a longer length is a caller error: truncated
   const int t_begin = split * p.split_len;
   if (t_begin >= ctx) return;  // no barriers in this kernel
   const int t_end = min(ctx, t_begin + p.split_len);
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams 
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= p.B * p.H) return;
   const int b = bh / p.H;
-  const int ctx = p.context_lens[b];
+  const int ctx = min(p.context_lens[b], p.max_ctx);  // a longer length is a caller error: truncated
   const int ns = (ctx + p.split_len - 1) / p.split_len;
   const int64_t base = (int64_t)bh * p.max_splits;
 

@@ -664,17 +664,25 @@ hipError_t launch_bf16_t(const FwdParams& p, hipStream_t s) {
   // SIMD (dense batches keep 64-key tiles: measured faster there, e.g. -10 % with 32-key
   // tiles on a causal 4 x 16 x 2048 batch, whose 1024 workgroups fill the chip in two
   // waves of two per CU)
-  if (VARLEN && CAUSAL && (int64_t)p.n_rb * kFwdBM <= kFwdShortLen) {
-    constexpr int BN = kFwdShortBN, WPE = kFwdShortWPE;
-    if (paged)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, WPE, CAUSAL, VARLEN, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, WPE, CAUSAL, VARLEN, false>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
-  } else if (paged) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, kFwdWPE, CAUSAL, VARLEN, VARLEN>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, kFwdWPE, CAUSAL, VARLEN, false>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+  // (compile-time branches: only causal varlen instantiates the 32-key configuration,
+  // only varlen the paged one)
+  if constexpr (VARLEN && CAUSAL) {
+    if ((int64_t)p.n_rb * kFwdBM <= kFwdShortLen) {
+      constexpr int BN = kFwdShortBN, WPE = kFwdShortWPE;
+      if (paged)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, WPE, CAUSAL, true, true>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+      else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, WPE, CAUSAL, true, false>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+      return hipGetLastError();
+    }
   }
+  if constexpr (VARLEN) {
+    if (paged) {
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, kFwdWPE, CAUSAL, true, true>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, kFwdBN, kFwdWPE, CAUSAL, VARLEN, false>), dim3((unsigned)nblk), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

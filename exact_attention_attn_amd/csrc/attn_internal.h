@@ -56,6 +56,7 @@ struct DecodeParams {
   int page_size;
   int split_len;        // tokens per split, a multiple of 16
   int max_splits;
+  int max_ctx;          // context lengths are clamped to this (max_context_len)
   float scale_log2;
 };
 

@@ -135,7 +135,10 @@ size_t attn_decode_paged_workspace_size(int B, int H, int d, int max_context_len
  *        ceil(context_lens[b] / page_size) are never read.
  * context_lens : int32 [B], each in [0, max_context_len]; sequence b's query attends
  *        its keys [0, context_lens[b]) (with one query token, causal and non-causal
- *        coincide).  Slots past the context in the last page are never read.
+ *        coincide).  Slots past the context in the last page are never read.  A length
+ *        above max_context_len is a caller error: the kernels truncate it to
+ *        max_context_len (no read outside the block-table row or the workspace); a
+ *        length of zero or below gives O = 0 and lse = -inf.
  * page_size : a positive multiple of 16.
  * lse  : float32 [B, H], or NULL.
  * workspace : device buffer of at least attn_decode_paged_workspace_size(...) bytes,

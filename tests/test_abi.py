@@ -250,3 +250,23 @@ def test_bwd_varlen_rejects_before_launch(kw, status):
 def test_bwd_varlen_workspace_size():
     assert attn.attn_bwd_varlen_workspace_size(300, 4) == 300 * 4 * 8
     assert attn.attn_bwd_varlen_workspace_size(0, 4) == 0
+
+
+def test_binding_refuses_host_tensors():
+    """The binding raises before the library is called when a tensor argument is not in
+    GPU memory (a host address given to a kernel would fault the device)."""
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_fwd(q, q, q)
+    x = torch.zeros((8, 1, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_fwd_varlen(x, x, x, cu, cu, 8, 8)
+    kc = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_decode_paged(torch.zeros((1, 1, 64), dtype=torch.bfloat16), kc, kc,
+                               torch.zeros((1, 2), dtype=torch.int32), torch.ones(1, dtype=torch.int32), 1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_store_kvcache(x[:, :, :], x, torch.zeros((1, 16, 1, 64), dtype=torch.bfloat16),
+                                torch.zeros((1, 16, 1, 64), dtype=torch.bfloat16), torch.zeros(8, dtype=torch.int64))

@@ -1,8 +1,10 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on the same
 seeded inputs, element by element.  bf16 runs feed the oracle the same bf16 values.
 
-Small shapes are compared everywhere; the full workloads are compared on sampled
-rows the oracle computes one by one, in the launch configuration the bench times.
+Small shapes are compared everywhere.  The five workloads (and the paged-prefill and
+grouped-query decode workloads the bench also times) are compared in full: every
+output element of every (batch, head) pair, in the launch configuration the bench
+times.  Only the 65536-row causal sequence is compared on sampled rows.
 """
 import math
 
@@ -86,19 +88,23 @@ def _rows(N, rng, extra=48):
     return np.array(sorted(r))
 
 
-def test_c2_bf16_full_sampled(A):
+def test_c2_bf16_full(A):
+    """Batched 4 x 16 x 2048 x 128 non-causal: all 64 (b, h) pairs, every row."""
     w = synth.workload("c2")
-    rng = np.random.default_rng(100)
-    pairs = [(0, 0), (1, 7), (2, 15), (3, 3)]
-    _dense_sampled(A, w, pairs, _rows(w.N, rng))
+    o, lse = run_dense(A, w)
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
-def test_c3_bf16_causal_full_sampled(A):
+def test_c3_bf16_causal_full(A):
+    """Causal 1 x 32 x 8192 x 128 (the headline workload): all 32 heads, every row."""
     w = synth.workload("c3")
-    rng = np.random.default_rng(101)
-    pairs = [(0, 0), (0, 13), (0, 31)]
-    o, lse = _dense_sampled(A, w, pairs, _rows(w.N, rng))
+    o, lse = run_dense(A, w)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_dense(w.q, w.k, w.v, w.scale, w.causal)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
 def test_dense_long_sequence_sampled(A):
@@ -110,19 +116,18 @@ def test_dense_long_sequence_sampled(A):
     assert np.isfinite(o).all() and np.isfinite(lse).all()
 
 
-def test_c4_varlen_full_sampled(A):
+def test_c4_varlen_full(A):
+    """16 packed causal sequences (34069 tokens, H = 32): every sequence, head and row."""
     import torch
     w = synth.workload("c4")
     o, lse = A.attn_fwd_varlen(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_q), dev(w.cu_k), w.max_q, w.max_k,
                                scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
-    rng = np.random.default_rng(102)
-    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, heads=[0, 17, 31],
-                                     rows_per_seq=lambda s, L: _rows(L, rng, 12))
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_varlen(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal)
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
-    assert np.isfinite(o).all()
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -143,6 +148,8 @@ def test_varlen_long_causal_sampled(A, d):
 
 
 def test_c5_decode_full(A):
+    """64 sequences over the paged pool (NaN poison page and tail slots): every
+    sequence and head."""
     import torch
     w = synth.workload("c5")
     o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
@@ -150,8 +157,7 @@ def test_c5_decode_full(A):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     assert np.isfinite(o).all() and np.isfinite(lse).all()   # no NaN page or tail slot was read
-    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale,
-                                           heads=[0, 9, 31])
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
@@ -414,9 +420,9 @@ def test_decode_gqa(A, H, Hkv, d, page):
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
-def test_gqa_decode_full_sampled(A):
+def test_gqa_decode_full(A):
     """The grouped-query decode workload the bench times (64 sequences, 16 query heads
-    on 8 KV heads), every sequence, sampled heads."""
+    on 8 KV heads): every sequence and head."""
     import torch
     w = synth.workload("gqa_decode")
     o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
@@ -424,8 +430,7 @@ def test_gqa_decode_full_sampled(A):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale,
-                                           heads=[0, 1, 7, 14, 15])
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
@@ -560,44 +565,56 @@ def test_paged_prefill_equals_contiguous_varlen(A):
     assert np.array_equal(host(o1), host(o2)) and np.array_equal(host(l1), host(l2))
 
 
-def test_prefill_paged_full_sampled(A):
+def test_prefill_paged_full(A):
     """The paged prefill the bench times: 16 sequences, the second half of each as new
-    causal query rows over its whole context in 16-token pages."""
+    causal query rows over its whole context in 16-token pages; every sequence, head
+    and row."""
     w = synth.workload("prefill_paged")
     o, lse = _run_prefill(A, w)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    rng = np.random.default_rng(103)
     ro, rl = oracle.attention_varlen_paged(w.q, w.k_cache, w.v_cache, w.cu_q, w.cu_k, w.block_table, w.scale,
-                                           True, heads=[0, 19, 31], rows_per_seq=lambda s, L: _rows(L, rng, 8))
+                                           True)
     assert_close("O", o, ro, TOL_BF16_O)
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
 # ------------------------------------------------------------------ backward
 
-# Gradient tolerance (none is stated for gradients): dQ, dK, dV are written in bf16
-# (relative rounding 2^-9) from fp32 sums whose terms use bf16 P, dS and O (2^-9 each),
-# so each source is about 2e-3 of the largest entries; the bound is ten times that.
-TOL_BWD_REL = 2e-2   # max-abs error over max |reference| per gradient tensor
-
-
-def _bwd_case(A, B, H, Hkv, N, Nk, d, causal, seed):
-    import torch
-    w = synth.dense(B, H, N, d, "bf16", causal, seed=seed, Nk=Nk, H_kv=Hkv)
-    do = synth.normal(seed, synth.T_DO, (B, H, N, d), True)
-    q, k, v = dev(w.q), dev(w.k), dev(w.v)
-    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=causal)
-    dq, dk, dv = A.attn_bwd(q, k, v, o, lse, dev(do), scale=w.scale, causal=causal)
-    torch.cuda.synchronize()
-    return w, do, host(dq), host(dk), host(dv)
+# Gradient tolerance (none is stated for gradients; derived here).  dQ, dK, dV are
+# written in bf16, whose round-to-nearest-even error is at most 2^-8 = 3.9e-3 of the
+# entry itself, from fp32 sums whose terms carry bf16 roundings of P and dS (2^-8
+# relative each, random in sign, so their sum's error is about 2^-8 / sqrt(3) of the
+# row's own magnitude) and the forward's bf16 O inside D = rowsum(dO * O).  Each
+# gradient ROW (one query row of dQ, one key row of dK or dV, per head) is therefore
+# held to a bound on its own scale: max-abs error <= TOL_BWD_ROW x max |reference row|
+# + TOL_BWD_FLOOR x max |reference tensor|.  The floor covers rows whose reference is
+# zero or nearly so (the first causal row's dQ is exactly 0: P = 1 and dP = D there),
+# where only the fp32 summation order is left.  The whole tensor is also held to
+# TOL_BWD_REL x max |reference|.
+TOL_BWD_REL = 1e-2     # whole tensor
+TOL_BWD_ROW = 2e-2     # per row, relative to the row's own max |reference|
+TOL_BWD_FLOOR = 1e-3   # per row, relative to the tensor's max |reference|
 
 
 def _assert_grad(name, got, want):
+    """``got``/``want`` [..., rows, d]: the last axis is one gradient row."""
     scale = max(1e-30, float(np.abs(want).max()))
     err, where, _ = max_err(got, want)
-    print(f"  {name}: max|err| = {err:.3e} at {where}, max|ref| = {scale:.3e}, rel {err / scale:.2e}", flush=True)
     assert np.isfinite(got).all(), f"{name}: non-finite entries"
+    g = got.reshape(-1, got.shape[-1])
+    w = want.reshape(-1, want.shape[-1])
+    row_err = np.abs(g - w).max(axis=1)
+    row_ref = np.abs(w).max(axis=1)
+    bound = TOL_BWD_ROW * row_ref + TOL_BWD_FLOOR * scale
+    worst = int(np.argmax(row_err / bound))
+    big = row_ref > 0.1 * scale   # rows of at least a tenth of the tensor's scale
+    rel_big = float((row_err[big] / row_ref[big]).max()) if big.any() else 0.0
+    print(f"  {name}: max|err| = {err:.3e} at {where}, max|ref| = {scale:.3e}, rel {err / scale:.2e}; "
+          f"worst row {worst}: err {row_err[worst]:.2e} ref {row_ref[worst]:.2e} ({row_err[worst] / bound[worst]:.2f} "
+          f"of its bound); rows >= 0.1 max: max err/ref {rel_big:.2e}", flush=True)
     assert err <= TOL_BWD_REL * scale, f"{name}: max|err| {err:.3e} > {TOL_BWD_REL} x {scale:.3e}"
+    assert row_err[worst] <= bound[worst], (f"{name}: row {worst} max|err| {row_err[worst]:.3e} > "
+                                            f"{TOL_BWD_ROW} x {row_ref[worst]:.3e} + {TOL_BWD_FLOOR} x {scale:.3e}")
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,Nk,d,causal", [
