@@ -10,16 +10,19 @@ from ._lib import (  # noqa: F401
     ATTN_DTYPE_F32,
     ATTN_ERR_INVALID_ARG,
     ATTN_ERR_LAUNCH,
+    ATTN_ERR_SCRATCH_LIMIT,
     ATTN_ERR_UNSUPPORTED,
     ATTN_OK,
     EXPORTS,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     AttnError,
     attn_bwd,
     attn_bwd_workspace_size,
     attn_bwd_varlen,
     attn_bwd_varlen_workspace_size,
     attn_decode_paged,
+    attn_decode_paged_noalloc,
     attn_decode_paged_workspace_size,
     attn_fwd,
     attn_fwd_varlen,

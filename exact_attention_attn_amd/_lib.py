@@ -14,10 +14,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
-ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH = 0, 1, 2, 3
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_LAUNCH, ATTN_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_decode_paged_workspace_size",
+           "attn_decode_paged_noalloc",
            "attn_store_kvcache", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_varlen",
            "attn_bwd_varlen_workspace_size", "attn_status_string", "attn_version")
 
@@ -48,6 +50,9 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                              vp]
+    lib.attn_decode_paged_noalloc.restype = i32
     i64 = ctypes.c_int64
     lib.attn_store_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, i32, vp]
     lib.attn_store_kvcache.restype = i32
@@ -256,6 +261,40 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "attn_decode_paged")
     return o, (lse if with_lse else None)
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, context_lens, max_context_len: int, out,
+                              scale: float | None = None, lse=None, stream=None):
+    """attn_decode_paged through the library's fixed device scratch: no workspace, and
+    nothing is allocated here either (``out`` [B, H, d] and the optional ``lse``
+    float32 [B, H] are the caller's).  Raises AttnError (ATTN_ERR_SCRATCH_LIMIT) when the
+    batch needs more than NOALLOC_SCRATCH_BYTES of split partials.  Calls that overlap on
+    one GPU share its scratch and race.  Returns (out, lse)."""
+    torch = _torch()
+    lib = load()
+    B, H, d = q.shape
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [num_pages, page, H_kv, d] matching q")
+    for t in (q, k_cache, v_cache, block_table, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_table and context_lens must be int32")
+    if out is None:
+        raise ValueError("attn_decode_paged_noalloc: out must be given (nothing is allocated)")
+    _on_device("attn_decode_paged_noalloc", q.device, q=q, k_cache=k_cache, v_cache=v_cache,
+               block_table=block_table, context_lens=context_lens, out=out, lse=lse)
+    _check_out("attn_decode_paged_noalloc", "out", out, (B, H, d), q.dtype)
+    _check_out("attn_decode_paged_noalloc", "lse", lse, (B, H), torch.float32)
+    if context_lens.numel() != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("context_lens must be [B] and block_table [B, max_pages]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib.attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                       _ptr(block_table), block_table.shape[1], _ptr(context_lens), B, num_pages,
+                                       page, H, Hkv, d, int(max_context_len), scale, _stream(stream))
+    _check(rc, "attn_decode_paged_noalloc")
+    return out, lse
 
 
 def attn_store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None):

@@ -54,6 +54,56 @@ inline int n_splits(int max_ctx) { return (max_ctx + attn::kDecodeSplit - 1) / a
 // Grouped-query heads: H_kv in [1, H] and dividing H (H == 0 launches nothing).
 inline bool heads_ok(int H, int H_kv) { return H == 0 || (H_kv >= 1 && H_kv <= H && H % H_kv == 0); }
 
+// Argument checks shared by the two paged-decode entries (host only: no device call).
+// *nothing is set when there is nothing to launch (B * H == 0).
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const void* o, const float* lse,
+                 const int32_t* block_table, int max_pages_per_seq, const int32_t* context_lens, int B,
+                 int num_pages, int page_size, int H, int H_kv, int d, int max_context_len, float scale,
+                 bool* nothing) {
+  *nothing = false;
+  if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0 || max_context_len < 0)
+    return fail(ATTN_ERR_INVALID_ARG);
+  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
+  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
+  if (page_size <= 0 || (page_size % 16) != 0) return fail(ATTN_ERR_UNSUPPORTED);
+  if ((int64_t)B * H == 0) {
+    *nothing = true;
+    return ATTN_OK;
+  }
+  if (!q || !o || !context_lens) return fail(ATTN_ERR_INVALID_ARG);
+  if (!aligned16(q) || !aligned16(o)) return fail(ATTN_ERR_UNSUPPORTED);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
+  if (max_context_len > 0) {
+    if (!k_cache || !v_cache || !block_table) return fail(ATTN_ERR_INVALID_ARG);
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(ATTN_ERR_UNSUPPORTED);
+    if ((int64_t)max_pages_per_seq * page_size < max_context_len) return fail(ATTN_ERR_INVALID_ARG);
+  }
+  return ATTN_OK;
+}
+
+// Launch of a checked paged decode with its split partials in `workspace`.
+int decode_launch(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                  const int32_t* block_table, int max_pages_per_seq, const int32_t* context_lens, int B,
+                  int page_size, int H, int H_kv, int d, int max_context_len, float scale, void* workspace,
+                  void* stream) {
+  attn::DecodeParams p{};
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.o = o; p.lse = lse;
+  p.block_table = block_table; p.context_lens = context_lens;
+  p.B = B; p.H = H; p.H_kv = H_kv; p.max_pages = max_pages_per_seq; p.page_size = page_size;
+  p.split_len = attn::kDecodeSplit;
+  p.max_ctx = max_context_len;
+  p.max_splits = max_context_len > 0 ? n_splits(max_context_len) : 0;
+  const size_t slots = (size_t)B * H * p.max_splits;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_acc ? p.ws_acc + slots * d : nullptr;
+  p.scale_log2 = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return check_launch(attn::launch_decode_paged(p, d, s), s);
+}
+
+static_assert(attn::kNoAllocScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "scratch size of include/attn.h");
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +116,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_SCRATCH_LIMIT: return "needs more scratch than the fixed device array of the no-allocation entry holds";
     default: return "unknown status";
   }
 }
@@ -174,38 +225,31 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
                       const int32_t* context_lens, int B, int num_pages, int page_size,
                       int H, int H_kv, int d, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || H < 0 || num_pages < 0 || max_pages_per_seq < 0 || max_context_len < 0)
-    return fail(ATTN_ERR_INVALID_ARG);
-  if (!heads_ok(H, H_kv)) return fail(ATTN_ERR_INVALID_ARG);
-  if (!scale_ok(scale)) return fail(ATTN_ERR_INVALID_ARG);
-  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED);
-  if (page_size <= 0 || (page_size % 16) != 0) return fail(ATTN_ERR_UNSUPPORTED);
-  if ((int64_t)B * H == 0) return ATTN_OK;
-  if (!q || !o || !context_lens) return fail(ATTN_ERR_INVALID_ARG);
-  if (!aligned16(q) || !aligned16(o)) return fail(ATTN_ERR_UNSUPPORTED);
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG);
-  if (max_context_len > 0) {
-    if (!k_cache || !v_cache || !block_table) return fail(ATTN_ERR_INVALID_ARG);
-    if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(ATTN_ERR_UNSUPPORTED);
-    if ((int64_t)max_pages_per_seq * page_size < max_context_len) return fail(ATTN_ERR_INVALID_ARG);
-  }
+  bool nothing = false;
+  const int rc = decode_check(q, k_cache, v_cache, o, lse, block_table, max_pages_per_seq, context_lens, B,
+                              num_pages, page_size, H, H_kv, d, max_context_len, scale, &nothing);
+  if (rc != ATTN_OK || nothing) return rc;
   const size_t need = attn_decode_paged_workspace_size(B, H, d, max_context_len, page_size);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(ATTN_ERR_INVALID_ARG);
+  return decode_launch(q, k_cache, v_cache, o, lse, block_table, max_pages_per_seq, context_lens, B, page_size, H,
+                       H_kv, d, max_context_len, scale, workspace, stream);
+}
 
-  attn::DecodeParams p{};
-  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.o = o; p.lse = lse;
-  p.block_table = block_table; p.context_lens = context_lens;
-  p.B = B; p.H = H; p.H_kv = H_kv; p.max_pages = max_pages_per_seq; p.page_size = page_size;
-  p.split_len = attn::kDecodeSplit;
-  p.max_ctx = max_context_len;
-  p.max_splits = max_context_len > 0 ? n_splits(max_context_len) : 0;
-  const size_t slots = (size_t)B * H * p.max_splits;
-  p.ws_acc = static_cast<float*>(workspace);
-  p.ws_ml = p.ws_acc ? p.ws_acc + slots * d : nullptr;
-  p.scale_log2 = scale * kLog2e;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return check_launch(attn::launch_decode_paged(p, d, s), s);
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, int B, int num_pages, int page_size,
+                              int H, int H_kv, int d, int max_context_len, float scale, void* stream) {
+  bool nothing = false;
+  const int rc = decode_check(q, k_cache, v_cache, o, lse, block_table, max_pages_per_seq, context_lens, B,
+                              num_pages, page_size, H, H_kv, d, max_context_len, scale, &nothing);
+  if (rc != ATTN_OK || nothing) return rc;
+  const size_t need = attn_decode_paged_workspace_size(B, H, d, max_context_len, page_size);
+  if (need > attn::kNoAllocScratchBytes) return fail(ATTN_ERR_SCRATCH_LIMIT);
+  void* ws = nullptr;
+  if (need > 0 && attn::noalloc_scratch(&ws) != hipSuccess) return fail(ATTN_ERR_LAUNCH);
+  return decode_launch(q, k_cache, v_cache, o, lse, block_table, max_pages_per_seq, context_lens, B, page_size, H,
+                       H_kv, d, max_context_len, scale, ws, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N) {

@@ -26,6 +26,8 @@
 #include "attn_internal.h"
 #include "attn_tile.h"
 
+#include <mutex>
+
 namespace attn {
 namespace {
 
@@ -492,6 +494,37 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s) {
   return d == 128 ? launch_t<128>(p, s) : launch_t<64>(p, s);
+}
+
+// ----------------------------------------------------------------------------------
+// Fixed scratch of the no-allocation decode entry: the split partials (acc, m, l) of one
+// call, for callers that cannot allocate device memory.  Every GPU the library runs on
+// holds its own copy of the array until the process ends; every call on a GPU reuses it
+// (calls that overlap in time on one GPU race).  In host code `scratch` names only a
+// host-side stand-in: its device address is looked up per device and kept.
+// ----------------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {  // with device `dev` current
+    void* a = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = a;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 }  // namespace attn

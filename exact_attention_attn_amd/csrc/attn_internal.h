@@ -99,6 +99,13 @@ struct BwdParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool varlen, hipStream_t s);  // paged iff p.block_table
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int d, hipStream_t s);
+
+// Bytes of the fixed device scratch array used by attn_decode_paged_noalloc (one per GPU,
+// held for the life of the process; the ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of the current device's scratch array.  The first call on a device
+// looks it up with that device current; later calls return the kept pointer.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_store_kvcache(const StoreParams& p, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool varlen, hipStream_t s);
 

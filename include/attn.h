@@ -64,8 +64,12 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale, short workspace */
   ATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (d, dtype, alignment, page size) */
-  ATTN_ERR_LAUNCH = 3       /* the HIP runtime reported an error at launch */
+  ATTN_ERR_LAUNCH = 3,      /* the HIP runtime reported an error at launch */
+  ATTN_ERR_SCRATCH_LIMIT = 4 /* attn_decode_paged_noalloc: the batch needs more than its fixed scratch */
 } attn_status;
+
+/* Bytes of the fixed device scratch array of attn_decode_paged_noalloc (one per GPU). */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
 
@@ -150,6 +154,30 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, v
                       const int32_t* context_lens, int B, int num_pages, int page_size,
                       int H, int H_kv, int d, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc — attn_decode_paged without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The call allocates and frees
+ * nothing; the caller still passes every input and output (same meaning, layout and
+ * ownership as attn_decode_paged, and the same results bit for bit).
+ *
+ * The split partials go to a fixed device array inside the library,
+ * ATTN_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held by each GPU the library runs on until
+ * the process ends.  Limit: attn_decode_paged_workspace_size(B, H, d, max_context_len,
+ * page_size) must not exceed it (at d = 128: B * H * ceil(max_context_len / 512) split
+ * slots of 520 bytes, at most 129055), else ATTN_ERR_SCRATCH_LIMIT is returned before any
+ * launch.  Nothing in the array needs to start at zero.
+ * Every call on a GPU shares that GPU's array and leaves its partials there: calls that
+ * overlap in time on one GPU (on different streams or from different host threads)
+ * race, and the caller must serialise them.
+ * The first call on a device looks up the array's device address (once per device, with
+ * that device current); `stream` must belong to the current device.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              const int32_t* context_lens, int B, int num_pages, int page_size,
+                              int H, int H_kv, int d, int max_context_len, float scale, void* stream);
 
 /*
  * attn_store_kvcache — write one step's new K/V rows into the paged pools.

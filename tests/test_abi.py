@@ -138,6 +138,45 @@ def test_decode_rejects_before_launch(kw, status):
     assert decode(**kw) == status
 
 
+def decode_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, lse=None, bt=FAKE, maxp=8, cl=FAKE, B=2, P=16, page=16, H=2,
+             Hkv=2, d=128, maxctx=128, scale=0.1)
+    a.update(kw)
+    return attn.load().attn_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["bt"], a["maxp"],
+                                                 a["cl"], a["B"], a["P"], a["page"], a["H"], a["Hkv"], a["d"],
+                                                 a["maxctx"], a["scale"], None)
+
+
+# d = 128: 520 bytes of partials per (sequence, head, 512-token split)
+_SLOTS = attn.NOALLOC_SCRATCH_BYTES // 520
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(bt=None), attn.ATTN_ERR_INVALID_ARG),
+    (dict(maxp=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), attn.ATTN_OK),
+    # one split slot past the fixed scratch: B * H * splits = _SLOTS + 1
+    (dict(B=_SLOTS + 1, H=1, Hkv=1, maxctx=512, maxp=32), attn.ATTN_ERR_SCRATCH_LIMIT),
+    (dict(B=4, H=32, Hkv=8, maxctx=512 * (_SLOTS // 128 + 1), maxp=32 * (_SLOTS // 128 + 1)),
+     attn.ATTN_ERR_SCRATCH_LIMIT),
+])
+def test_decode_noalloc_rejects_before_launch(kw, status):
+    """The no-allocation decode entry checks its arguments like attn_decode_paged and
+    refuses a batch whose split partials exceed its fixed scratch, before any launch."""
+    assert decode_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_header():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in src
+    assert attn.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert attn.status_string(attn.ATTN_ERR_SCRATCH_LIMIT).startswith("needs more scratch")
+
+
 def test_workspace_size():
     ws = attn.attn_decode_paged_workspace_size
     assert ws(0, 32, 128, 8192, 16) == 0
