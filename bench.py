@@ -222,70 +222,97 @@ def main() -> int:
     attn.load()
     dev_name = torch.cuda.get_device_name(0)
 
+    # legs to run and the workloads they need (only those are generated)
+    step_names = ["fwd", "varlen", "decode"]
+    extra_names = ["c1", "c2", "decode_gqa", "store_kvcache", "prefill_paged", "bwd", "bwd_varlen"]
+    if args.only:
+        step_names = [n for n in step_names if n == args.only]
+        extra_names = [n for n in extra_names if n == args.only]
+    need = set(step_names + extra_names)
+    with_cpu = not args.no_cpu_baseline and "fwd" in need
+    if with_cpu:
+        need |= {"c1", "c2", "fwd", "varlen", "decode"}
+    if "bwd" in need:
+        need.add("fwd")
+    if "bwd_varlen" in need:
+        need.add("varlen")
+
     t = time.perf_counter()
-    w1 = synth.workload("c1")
-    q1, k1, v1 = dev(w1.q), dev(w1.k), dev(w1.v)
-    o1 = torch.empty_like(q1)
-    l1 = torch.empty((1, 1, w1.N), dtype=torch.float32, device="cuda")
-    w2 = synth.workload("c2")
-    q2, k2, v2 = dev(w2.q), dev(w2.k), dev(w2.v)
-    o2 = torch.empty_like(q2)
-    l2 = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device="cuda")
-    w3 = synth.workload("c3")
-    q3, k3, v3 = dev(w3.q), dev(w3.k), dev(w3.v)
-    o3 = torch.empty_like(q3)
-    l3 = torch.empty((1, 32, 8192), dtype=torch.float32, device="cuda")
-    log(f"[bench] dense workload ready ({time.perf_counter() - t:.1f} s)")
+    if "c1" in need:
+        w1 = synth.workload("c1")
+        q1, k1, v1 = dev(w1.q), dev(w1.k), dev(w1.v)
+        o1 = torch.empty_like(q1)
+        l1 = torch.empty((1, 1, w1.N), dtype=torch.float32, device="cuda")
+    if "c2" in need:
+        w2 = synth.workload("c2")
+        q2, k2, v2 = dev(w2.q), dev(w2.k), dev(w2.v)
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((w2.B, w2.H, w2.N), dtype=torch.float32, device="cuda")
+    if "fwd" in need:
+        w3 = synth.workload("c3")
+        q3, k3, v3 = dev(w3.q), dev(w3.k), dev(w3.v)
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty((1, 32, 8192), dtype=torch.float32, device="cuda")
+    log(f"[bench] dense workloads ready ({time.perf_counter() - t:.1f} s)")
 
-    w4 = synth.workload("c4")
-    q4, k4, v4 = dev(w4.q), dev(w4.k), dev(w4.v)
-    cq4, ck4 = dev(w4.cu_q), dev(w4.cu_k)
-    o4 = torch.empty_like(q4)
-    l4 = torch.empty((q4.shape[0], 32), dtype=torch.float32, device="cuda")
-    log(f"[bench] varlen workload ready ({time.perf_counter() - t:.1f} s)")
+    if "varlen" in need:
+        w4 = synth.workload("c4")
+        q4, k4, v4 = dev(w4.q), dev(w4.k), dev(w4.v)
+        cq4, ck4 = dev(w4.cu_q), dev(w4.cu_k)
+        o4 = torch.empty_like(q4)
+        l4 = torch.empty((q4.shape[0], 32), dtype=torch.float32, device="cuda")
+        log(f"[bench] varlen workload ready ({time.perf_counter() - t:.1f} s)")
 
-    w5 = synth.workload("c5")
-    q5, kc5, vc5 = dev(w5.q), dev(w5.k_cache), dev(w5.v_cache)
-    bt5, cl5 = dev(w5.block_table), dev(w5.context_lens)
-    maxctx5 = int(w5.context_lens.max())
-    ws5 = torch.empty(attn.attn_decode_paged_workspace_size(64, 32, 128, maxctx5, 16), dtype=torch.uint8, device="cuda")
-    o5 = torch.empty_like(q5)
-    l5 = torch.empty((64, 32), dtype=torch.float32, device="cuda")
-    # (the host copies stay: the oracle's timed sample reads them)
-    log(f"[bench] decode workload ready ({time.perf_counter() - t:.1f} s)")
+    if "decode" in need:
+        w5 = synth.workload("c5")
+        q5, kc5, vc5 = dev(w5.q), dev(w5.k_cache), dev(w5.v_cache)
+        bt5, cl5 = dev(w5.block_table), dev(w5.context_lens)
+        maxctx5 = int(w5.context_lens.max())
+        ws5 = torch.empty(attn.attn_decode_paged_workspace_size(64, 32, 128, maxctx5, 16), dtype=torch.uint8,
+                          device="cuda")
+        o5 = torch.empty_like(q5)
+        l5 = torch.empty((64, 32), dtype=torch.float32, device="cuda")
+        # (the host copies stay: the oracle's timed sample reads them)
+        log(f"[bench] decode workload ready ({time.perf_counter() - t:.1f} s)")
 
-    w6 = synth.workload("gqa_decode")
-    q6, kc6, vc6 = dev(w6.q), dev(w6.k_cache), dev(w6.v_cache)
-    bt6, cl6 = dev(w6.block_table), dev(w6.context_lens)
-    maxctx6 = int(w6.context_lens.max())
-    ws6 = torch.empty(attn.attn_decode_paged_workspace_size(64, 16, 128, maxctx6, 16), dtype=torch.uint8, device="cuda")
-    o6 = torch.empty_like(q6)
-    l6 = torch.empty((64, 16), dtype=torch.float32, device="cuda")
-    w6.k_cache = w6.v_cache = None
-    log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
+    if "decode_gqa" in need:
+        w6 = synth.workload("gqa_decode")
+        q6, kc6, vc6 = dev(w6.q), dev(w6.k_cache), dev(w6.v_cache)
+        bt6, cl6 = dev(w6.block_table), dev(w6.context_lens)
+        maxctx6 = int(w6.context_lens.max())
+        ws6 = torch.empty(attn.attn_decode_paged_workspace_size(64, 16, 128, maxctx6, 16), dtype=torch.uint8,
+                          device="cuda")
+        o6 = torch.empty_like(q6)
+        l6 = torch.empty((64, 16), dtype=torch.float32, device="cuda")
+        w6.k_cache = w6.v_cache = None
+        log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
 
-    w8 = synth.workload("prefill_paged")
-    q8, kc8, vc8 = dev(w8.q), dev(w8.k_cache), dev(w8.v_cache)
-    cq8, ck8, bt8 = dev(w8.cu_q), dev(w8.cu_k), dev(w8.block_table)
-    o8 = torch.empty_like(q8)
-    l8 = torch.empty((q8.shape[0], 32), dtype=torch.float32, device="cuda")
-    w8.k_cache = w8.v_cache = None
-    log(f"[bench] paged prefill workload ready ({time.perf_counter() - t:.1f} s)")
+    if "prefill_paged" in need:
+        w8 = synth.workload("prefill_paged")
+        q8, kc8, vc8 = dev(w8.q), dev(w8.k_cache), dev(w8.v_cache)
+        cq8, ck8, bt8 = dev(w8.cu_q), dev(w8.cu_k), dev(w8.block_table)
+        o8 = torch.empty_like(q8)
+        l8 = torch.empty((q8.shape[0], 32), dtype=torch.float32, device="cuda")
+        w8.k_cache = w8.v_cache = None
+        log(f"[bench] paged prefill workload ready ({time.perf_counter() - t:.1f} s)")
 
-    do3 = dev(synth.normal(0, synth.T_DO, (1, 32, 8192, 128), True))
-    dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
-    wsb = torch.empty(attn.attn_bwd_workspace_size(1, 32, 8192), dtype=torch.uint8, device="cuda")
-    log(f"[bench] backward workload ready ({time.perf_counter() - t:.1f} s)")
+    if "bwd" in need:
+        do3 = dev(synth.normal(0, synth.T_DO, (1, 32, 8192, 128), True))
+        dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+        wsb = torch.empty(attn.attn_bwd_workspace_size(1, 32, 8192), dtype=torch.uint8, device="cuda")
+        log(f"[bench] backward workload ready ({time.perf_counter() - t:.1f} s)")
 
-    do4 = dev(synth.normal(0, synth.T_DO, tuple(w4.q.shape), True))
-    dq4, dk4, dv4 = torch.empty_like(q4), torch.empty_like(k4), torch.empty_like(v4)
-    wsb4 = torch.empty(attn.attn_bwd_varlen_workspace_size(q4.shape[0], 32), dtype=torch.uint8, device="cuda")
-    log(f"[bench] varlen backward workload ready ({time.perf_counter() - t:.1f} s)")
+    if "bwd_varlen" in need:
+        do4 = dev(synth.normal(0, synth.T_DO, tuple(w4.q.shape), True))
+        dq4, dk4, dv4 = torch.empty_like(q4), torch.empty_like(k4), torch.empty_like(v4)
+        wsb4 = torch.empty(attn.attn_bwd_varlen_workspace_size(q4.shape[0], 32), dtype=torch.uint8, device="cuda")
+        log(f"[bench] varlen backward workload ready ({time.perf_counter() - t:.1f} s)")
 
-    w7 = synth.workload("store_prefill")
-    k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
-    sl7 = torch.from_numpy(w7.slot_mapping).cuda()
-    log(f"[bench] store_kvcache workload ready ({time.perf_counter() - t:.1f} s)")
+    if "store_kvcache" in need:
+        w7 = synth.workload("store_prefill")
+        k7, v7, kc7, vc7 = dev(w7.k), dev(w7.v), dev(w7.k_cache), dev(w7.v_cache)
+        sl7 = torch.from_numpy(w7.slot_mapping).cuda()
+        log(f"[bench] store_kvcache workload ready ({time.perf_counter() - t:.1f} s)")
 
     def run_fwd():
         attn.attn_fwd(q3, k3, v3, scale=w3.scale, causal=True, out=o3, lse=l3)
@@ -323,12 +350,11 @@ def main() -> int:
     # paged decode.  The further entry points (grouped-query decode, store_kvcache, paged
     # prefill, both backward passes) are timed after it, in a loop of their own of the
     # same length, so that their heat does not lower the clock under the step's legs.
-    parts = [("fwd", run_fwd), ("varlen", run_varlen), ("decode", run_decode)]
-    extra = [("c1", run_c1), ("c2", run_c2), ("decode_gqa", run_decode_gqa), ("store_kvcache", run_store), ("prefill_paged", run_prefill_paged),
-             ("bwd", run_bwd), ("bwd_varlen", run_bwd_varlen)]
-    if args.only:
-        parts = [p for p in parts if p[0] == args.only]
-        extra = [p for p in extra if p[0] == args.only]
+    fns = {"fwd": run_fwd, "varlen": run_varlen, "decode": run_decode, "c1": run_c1, "c2": run_c2,
+           "decode_gqa": run_decode_gqa, "store_kvcache": run_store, "prefill_paged": run_prefill_paged,
+           "bwd": run_bwd, "bwd_varlen": run_bwd_varlen}
+    parts = [(n, fns[n]) for n in step_names]
+    extra = [(n, fns[n]) for n in extra_names]
 
     def timed_loop(legs):
         """W warm-up rounds, then K timed rounds of `legs`, each call bracketed by HIP
@@ -365,8 +391,8 @@ def main() -> int:
     fl3 = fwd_flops_causal(32, 8192, 128)
     fl2 = 4.0 * 128 * 4 * 16 * 2048 * 2048
     fl1 = 4.0 * 64 * 256 * 256
-    fl4 = varlen_flops(w4.lens_q, 32, 128)
-    by5 = decode_bytes(w5.context_lens, 64, 32, 128, 16)
+    fl4 = varlen_flops(w4.lens_q, 32, 128) if "varlen" in need else None
+    by5 = decode_bytes(w5.context_lens, 64, 32, 128, 16) if "decode" in need else None
     res = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": ms_total / args.steps, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -446,7 +472,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 512 << 20
-    if not args.no_cpu_baseline and "fwd" in ms:
+    if with_cpu:
         # bounded samples: about 25 s of oracle work in all on the host's cores
         gpu = {n: float(ms[m].mean()) for n, m in (("c1", "c1"), ("c2", "c2"), ("c3", "fwd"), ("c4", "varlen"),
                                                    ("c5", "decode")) if m in ms}

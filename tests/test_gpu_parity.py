@@ -583,21 +583,38 @@ def test_prefill_paged_full(A):
 # Gradient tolerance (none is stated for gradients; derived here).  dQ, dK, dV are
 # written in bf16, whose round-to-nearest-even error is at most 2^-8 = 3.9e-3 of the
 # entry itself, from fp32 sums whose terms carry bf16 roundings of P and dS (2^-8
-# relative each, random in sign, so their sum's error is about 2^-8 / sqrt(3) of the
-# row's own magnitude) and the forward's bf16 O inside D = rowsum(dO * O).  Each
-# gradient ROW (one query row of dQ, one key row of dK or dV, per head) is therefore
-# held to a bound on its own scale: max-abs error <= TOL_BWD_ROW x max |reference row|
-# + TOL_BWD_FLOOR x max |reference tensor|.  The floor covers rows whose reference is
-# zero or nearly so (the first causal row's dQ is exactly 0: P = 1 and dP = D there),
-# where only the fp32 summation order is left.  The whole tensor is also held to
-# TOL_BWD_REL x max |reference|.
-TOL_BWD_REL = 1e-2     # whole tensor
-TOL_BWD_ROW = 2e-2     # per row, relative to the row's own max |reference|
-TOL_BWD_FLOOR = 1e-3   # per row, relative to the tensor's max |reference|
+# relative each, random in sign) and the forward's bf16 O inside D = rowsum(dO * O).
+# Whole tensor: max-abs error <= TOL_BWD_REL x max |reference| (measured at most 5.2e-3,
+# dQ, over every case below).  Each gradient ROW (a query row of dQ, a key row of dK or
+# dV, per head) is also held to a bound on its own scale,
+#     max-abs error <= row_tol x max |reference row| + floor x max |reference tensor|,
+# so that a wrong low-magnitude row (late causal keys, rows with few keys) fails even
+# when the tensor-wide bound would not see it.  dK and dV rows sum random-signed
+# rounding errors of their own terms.  dQ rows carry one more term: the rounding of D_i
+# enters every key of row i with the same sign (scale * dD_i * sum_j P_ij K_j), so it does
+# not shrink with the row's own magnitude (the first causal row's dQ is exactly 0, as
+# P = 1 and dP = D there); dQ gets the larger floor.  Needed over every case below
+# (row_tol at the given floor): dV 3.3e-3 and dK 6.6e-3 at 1e-3, dQ 2.5e-2 at 2e-3;
+# the bounds are 2-3 times that.
+TOL_BWD_REL = 1e-2
+TOL_BWD_ROWS = {"dQ": (5e-2, 2e-3), "dK": (2e-2, 1e-3), "dV": (1e-2, 1e-3)}   # (row_tol, floor)
+
+
+def _bwd_case(A, B, H, Hkv, N, Nk, d, causal, seed):
+    import torch
+    w = synth.dense(B, H, N, d, "bf16", causal, seed=seed, Nk=Nk, H_kv=Hkv)
+    do = synth.normal(seed, synth.T_DO, (B, H, N, d), True)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    o, lse = A.attn_fwd(q, k, v, scale=w.scale, causal=causal)
+    dq, dk, dv = A.attn_bwd(q, k, v, o, lse, dev(do), scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    return w, do, host(dq), host(dk), host(dv)
 
 
 def _assert_grad(name, got, want):
-    """``got``/``want`` [..., rows, d]: the last axis is one gradient row."""
+    """``got``/``want`` [..., rows, d]: the last axis is one gradient row; ``name`` starts
+    with dQ, dK or dV."""
+    row_tol, floor = TOL_BWD_ROWS[name[:2]]
     scale = max(1e-30, float(np.abs(want).max()))
     err, where, _ = max_err(got, want)
     assert np.isfinite(got).all(), f"{name}: non-finite entries"
@@ -605,16 +622,14 @@ def _assert_grad(name, got, want):
     w = want.reshape(-1, want.shape[-1])
     row_err = np.abs(g - w).max(axis=1)
     row_ref = np.abs(w).max(axis=1)
-    bound = TOL_BWD_ROW * row_ref + TOL_BWD_FLOOR * scale
+    bound = row_tol * row_ref + floor * scale
     worst = int(np.argmax(row_err / bound))
-    big = row_ref > 0.1 * scale   # rows of at least a tenth of the tensor's scale
-    rel_big = float((row_err[big] / row_ref[big]).max()) if big.any() else 0.0
     print(f"  {name}: max|err| = {err:.3e} at {where}, max|ref| = {scale:.3e}, rel {err / scale:.2e}; "
-          f"worst row {worst}: err {row_err[worst]:.2e} ref {row_ref[worst]:.2e} ({row_err[worst] / bound[worst]:.2f} "
-          f"of its bound); rows >= 0.1 max: max err/ref {rel_big:.2e}", flush=True)
+          f"worst row {worst}: err {row_err[worst]:.2e}, row max|ref| {row_ref[worst]:.2e}, "
+          f"{row_err[worst] / bound[worst]:.2f} of its bound", flush=True)
     assert err <= TOL_BWD_REL * scale, f"{name}: max|err| {err:.3e} > {TOL_BWD_REL} x {scale:.3e}"
     assert row_err[worst] <= bound[worst], (f"{name}: row {worst} max|err| {row_err[worst]:.3e} > "
-                                            f"{TOL_BWD_ROW} x {row_ref[worst]:.3e} + {TOL_BWD_FLOOR} x {scale:.3e}")
+                                            f"{row_tol} x {row_ref[worst]:.3e} + {floor} x {scale:.3e}")
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,Nk,d,causal", [
