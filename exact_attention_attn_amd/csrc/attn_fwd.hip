@@ -87,6 +87,41 @@ __device__ __forceinline__ void block_coords(const FwdParams& p, int& rb, int& b
   rb = CAUSAL ? (p.n_rb - 1 - rbi) : rbi;
 }
 
+// Dense causal launches: the row blocks of a head come in pairs (n_rb - 1 - j, j), one
+// pair per workgroup, so every workgroup does the same work (n_rb + 1 key tiles of 128
+// rows for a 128-row block), whatever the row block.  The hardware places workgroups on
+// the CUs in dispatch order without regard to their length, so with one row block per
+// workgroup the CUs that drew the long blocks of the diagonal ran on after the others;
+// equal pairs leave no such tail.  Block order as in block_coords (KV pairs round-robin
+// over the XCDs, the query heads of a KV head back to back).  rb1 == rb0 for the middle
+// block of an odd count.
+__device__ __forceinline__ void block_coords_pair(const FwdParams& p, int& rb0, int& rb1, int& b, int& h) {
+  const int G = p.kv_group;
+  const int hkv = p.H / G;
+  const int nkv = hkv * p.B;
+  const int npr = (p.n_rb + 1) >> 1;  // pairs per head
+  const int bid = blockIdx.x;
+  int j;
+  if ((nkv & 7) == 0) {
+    const int x = bid & 7, i = bid >> 3;
+    const int per = G * npr;
+    const int kvp = x + 8 * (i / per);
+    const int r = i - (i / per) * per;
+    const int member = r / npr;
+    j = r - member * npr;
+    b = kvp / hkv;
+    h = (kvp - b * hkv) * G + member;
+  } else {
+    const int npairs = p.H * p.B;
+    const int pair = bid % npairs;
+    j = bid / npairs;
+    b = pair / p.H;
+    h = pair - b * p.H;
+  }
+  rb0 = p.n_rb - 1 - j;
+  rb1 = j;
+}
+
 // Per-(sequence, head) extents and element offsets.  Paged K/V: koff / voff only select
 // the KV head inside a slot; the page comes from the block table per key.
 template <bool VARLEN, bool PAGED = false>
@@ -158,399 +193,416 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  int rb, b, h;
-  block_coords<CAUSAL>(p, rb, b, h);
+  // dense causal: two row blocks of equal total work per workgroup (block_coords_pair)
+  constexpr bool PAIRED = CAUSAL && !VARLEN;
+  int rbs[2], b, h;
+  if constexpr (PAIRED) {
+    block_coords_pair(p, rbs[0], rbs[1], b, h);
+  } else {
+    block_coords<CAUSAL>(p, rbs[0], b, h);
+    rbs[1] = rbs[0];
+  }
   int Lq, Lk;
   int64_t qoff, koff, voff, ooff, loff;
   seq_bounds<VARLEN, PAGED>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
-  const int row0 = rb * BM;
-  if (row0 >= Lq) return;  // uniform over the workgroup
 
-  const int shift = Lk - Lq;  // bottom-right causal alignment
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
-  const int ntiles = (kend + BN - 1) / BN;
-  // tiles [0, nfull) need no mask for any row of this workgroup
-  int nfull = Lk / BN;
-  if (CAUSAL) nfull = min(nfull, max(0, (row0 + shift + 1) / BN));
+  // One row block: its Q rows against every admissible K/V tile, then O and lse.
+  auto row_block = [&](const int rb) {
+    const int row0 = rb * BM;
+    if (row0 >= Lq) return;  // uniform over the workgroup
 
-  const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + qoff;
-  const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + koff;
-  const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + voff;
-  const int64_t ksn = p.k_sn, vsn = p.v_sn;
+    const int shift = Lk - Lq;  // bottom-right causal alignment
+    int kend = Lk;
+    if (CAUSAL) kend = min(Lk, max(0, row0 + BM + shift));
+    const int ntiles = (kend + BN - 1) / BN;
+    // tiles [0, nfull) need no mask for any row of this workgroup
+    int nfull = Lk / BN;
+    if (CAUSAL) nfull = min(nfull, max(0, (row0 + shift + 1) / BN));
 
-  const int wrow0 = row0 + wave * 32;
-  const int qi = wrow0 + col;
+    const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + qoff;
+    const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + koff;
+    const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + voff;
+    const int64_t ksn = p.k_sn, vsn = p.v_sn;
 
-  bf16x8 qreg[DT];
+    const int wrow0 = row0 + wave * 32;
+    const int qi = wrow0 + col;
+
+    bf16x8 qreg[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (qi < Lq) u = *(const u32x4*)(Qg + (int64_t)qi * p.q_sn + 16 * t + 8 * half);
-    qreg[t] = as_bf16x8(u);
-  }
-
-  // Per-lane source rows and in-row byte offsets of this wavefront's direct-to-LDS loads.
-  // In the last tile, rows past the sequence end are clamped to its last row: the
-  // direct-to-LDS path does not reliably write zeros for out-of-range rows, and stale LDS
-  // data times a zero probability could be NaN.  Clamped keys are masked to -inf.
-  int kkey[BPW], kcol[BPW], vkey[BPW], vcol[BPW], kdoff[BPW], vdoff[BPW];
-  const int krow_bytes = (int)ksn * 2, vrow_bytes = (int)vsn * 2;
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int bi = wave * BPW + i;
-    {  // K block bi = (key group g, chunk quad q): key 16 g + lane / 4, chunk
-       // 4 q + ((lane % 4) ^ ((lane / 16) % 4))
-      constexpr int NQ = D / 32;
-      const int g = bi / NQ, q = bi % NQ;
-      kkey[i] = 16 * g + (lane >> 2);
-      kcol[i] = (4 * q + ((lane & 3) ^ ((lane >> 4) & 3))) * 16;
+    for (int t = 0; t < DT; ++t) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (qi < Lq) u = *(const u32x4*)(Qg + (int64_t)qi * p.q_sn + 16 * t + 8 * half);
+      qreg[t] = as_bf16x8(u);
     }
-    {  // V block bi: column block bi / (BN / 16), keys 16 * (bi % (BN / 16)) + lane / 4, chunk lane % 4
-      const int db = bi / (BN / 16);
-      vkey[i] = 16 * (bi % (BN / 16)) + lane / 4;
-      vcol[i] = (32 * db + 8 * (lane % 4)) * 2;
-    }
-    kdoff[i] = kkey[i] * krow_bytes + kcol[i];
-    vdoff[i] = vkey[i] * vrow_bytes + vcol[i];
-  }
 
-  // Paged K/V: every 1 KiB load block covers one 16-key group of its tile, and a group
-  // lies in one page (page sizes are powers of two >= 16), so a block's source is a
-  // uniform base (its group's page, read from the block table one step before the load)
-  // plus a loop-invariant lane offset.  In the last tile, keys past the end are clamped
-  // to the last key, whose group then serves the whole block.
-  const int32_t* __restrict__ bt_row = PAGED ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
-  const int pshift = PAGED ? p.page_shift : 0;
-  const int pmask = (1 << pshift) - 1;
-  int kgrp[BPW], vgrp[BPW], kloff[BPW], vloff[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int bi = wave * BPW + i;
-    kgrp[i] = bi / (D / 32);
-    vgrp[i] = bi % (BN / 16);
-    kloff[i] = (kkey[i] & 15) * krow_bytes + kcol[i];
-    vloff[i] = (vkey[i] & 15) * vrow_bytes + vcol[i];
-  }
-  // Page of block i's group.  A wavefront's K blocks are the NQ chunk quads of one key
-  // group, so K needs one page per tile (entry 0); V blocks span the tile's groups.
-  static_assert(BPW <= D / 32 && (D / 32) % BPW == 0, "a wavefront's K blocks share one key group");
-  int kpg[1], vpg[PAGED ? BPW : 1];
-  // The page ids are uniform per wavefront: read through the constant address space,
-  // they become scalar loads into SGPRs (no VGPRs: the 32-key, 3-wavefront configuration
-  // spilled with them in VGPRs) whose wait counter is not the one of the tile loads.
-  // They are issued a step ahead and pass through an empty asm right after the step's
-  // barrier, so that the compiler's wait for them lands there.
-  auto load_pages = [&](int j, const int* grp, int* pg, int n) {
-    const int kt0 = j * BN;
-    const int glast = (Lk - 1 - kt0) >> 4;  // last group holding a valid key
-#pragma unroll
-    for (int i = 0; i < BPW; ++i)
-      if (i < n)
-        pg[i] = *(const __attribute__((address_space(4))) int32_t*)(bt_row + ((kt0 + 16 * min(grp[i], glast)) >> pshift));
-  };
-  auto settle_pages = [&]() {
-    asm volatile("" : "+s"(kpg[0]));
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) asm volatile("" : "+s"(vpg[i]));
-  };
-  auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* grp, const int* loff,
-                         const int* key, const int* colb, const int* pg, bool one_page, int row_bytes) {
-    const int kt0 = j * BN;
-    const int last = Lk - kt0 - 1;
-    const int glast = last >> 4;
+    // Per-lane source rows and in-row byte offsets of this wavefront's direct-to-LDS loads.
+    // In the last tile, rows past the sequence end are clamped to its last row: the
+    // direct-to-LDS path does not reliably write zeros for out-of-range rows, and stale LDS
+    // data times a zero probability could be NaN.  Clamped keys are masked to -inf.
+    int kkey[BPW], kcol[BPW], vkey[BPW], vcol[BPW], kdoff[BPW], vdoff[BPW];
+    const int krow_bytes = (int)ksn * 2, vrow_bytes = (int)vsn * 2;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int geff = min(grp[i], glast);
-      const int page = pg[one_page ? 0 : i];  // scalar, loaded a step earlier
-      const uint8_t* gbase =
-          (const uint8_t*)base + (((int64_t)page << pshift) + ((kt0 + 16 * geff) & pmask)) * row_bytes;
-      const int vo = last >= BN - 1 ? loff[i] : (min(key[i], last) - 16 * geff) * row_bytes + colb[i];
-      dma16s(gbase, vo, buf + (wave * BPW + i) * 1024);
+      const int bi = wave * BPW + i;
+      {  // K block bi = (key group g, chunk quad q): key 16 g + lane / 4, chunk
+         // 4 q + ((lane % 4) ^ ((lane / 16) % 4))
+        constexpr int NQ = D / 32;
+        const int g = bi / NQ, q = bi % NQ;
+        kkey[i] = 16 * g + (lane >> 2);
+        kcol[i] = (4 * q + ((lane & 3) ^ ((lane >> 4) & 3))) * 16;
+      }
+      {  // V block bi: column block bi / (BN / 16), keys 16 * (bi % (BN / 16)) + lane / 4, chunk lane % 4
+        const int db = bi / (BN / 16);
+        vkey[i] = 16 * (bi % (BN / 16)) + lane / 4;
+        vcol[i] = (32 * db + 8 * (lane % 4)) * 2;
+      }
+      kdoff[i] = kkey[i] * krow_bytes + kcol[i];
+      vdoff[i] = vkey[i] * vrow_bytes + vcol[i];
     }
-  };
 
-  auto issue_k = [&](int j, uint8_t* kb) {
-    if (PAGED) {
-      issue_paged(j, kb, Kg, kgrp, kloff, kkey, kcol, kpg, true, krow_bytes);
-      return;
-    }
-    const int kt0 = j * BN;
-    const int last = Lk - kt0 - 1;  // last valid row of this tile (>= 0)
-    const int64_t krem = ((int64_t)last * ksn + D) * 2;  // bytes of valid keys from kt0 on
-    const u32x4s kr = buffer_rsrc(Kg + (int64_t)kt0 * ksn, krem);
-    if (last >= BN - 1) {
+    // Paged K/V: every 1 KiB load block covers one 16-key group of its tile, and a group
+    // lies in one page (page sizes are powers of two >= 16), so a block's source is a
+    // uniform base (its group's page, read from the block table one step before the load)
+    // plus a loop-invariant lane offset.  In the last tile, keys past the end are clamped
+    // to the last key, whose group then serves the whole block.
+    const int32_t* __restrict__ bt_row = PAGED ? p.block_table + (int64_t)b * p.bt_stride : nullptr;
+    const int pshift = PAGED ? p.page_shift : 0;
+    const int pmask = (1 << pshift) - 1;
+    int kgrp[BPW], vgrp[BPW], kloff[BPW], vloff[BPW];
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) dma16(kr, kb + (wave * BPW + i) * 1024, kdoff[i]);
-    } else {
+    for (int i = 0; i < BPW; ++i) {
+      const int bi = wave * BPW + i;
+      kgrp[i] = bi / (D / 32);
+      vgrp[i] = bi % (BN / 16);
+      kloff[i] = (kkey[i] & 15) * krow_bytes + kcol[i];
+      vloff[i] = (vkey[i] & 15) * vrow_bytes + vcol[i];
+    }
+    // Page of block i's group.  A wavefront's K blocks are the NQ chunk quads of one key
+    // group, so K needs one page per tile (entry 0); V blocks span the tile's groups.
+    static_assert(BPW <= D / 32 && (D / 32) % BPW == 0, "a wavefront's K blocks share one key group");
+    int kpg[1], vpg[PAGED ? BPW : 1];
+    // The page ids are uniform per wavefront: read through the constant address space,
+    // they become scalar loads into SGPRs (no VGPRs: the 32-key, 3-wavefront configuration
+    // spilled with them in VGPRs) whose wait counter is not the one of the tile loads.
+    // They are issued a step ahead and pass through an empty asm right after the step's
+    // barrier, so that the compiler's wait for them lands there.
+    auto load_pages = [&](int j, const int* grp, int* pg, int n) {
+      const int kt0 = j * BN;
+      const int glast = (Lk - 1 - kt0) >> 4;  // last group holding a valid key
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
-        dma16(kr, kb + (wave * BPW + i) * 1024, min(kkey[i], last) * krow_bytes + kcol[i]);
-    }
-  };
-  auto issue_v = [&](int j, uint8_t* vb) {
-    if (PAGED) {
-      issue_paged(j, vb, Vg, vgrp, vloff, vkey, vcol, vpg, false, vrow_bytes);
-      return;
-    }
-    const int kt0 = j * BN;
-    const int last = Lk - kt0 - 1;
-    const int64_t vrem = ((int64_t)last * vsn + D) * 2;
-    const u32x4s vr = buffer_rsrc(Vg + (int64_t)kt0 * vsn, vrem);
-    if (last >= BN - 1) {
+        if (i < n)
+          pg[i] = *(const __attribute__((address_space(4))) int32_t*)(bt_row + ((kt0 + 16 * min(grp[i], glast)) >> pshift));
+    };
+    auto settle_pages = [&]() {
+      asm volatile("" : "+s"(kpg[0]));
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) dma16(vr, vb + (wave * BPW + i) * 1024, vdoff[i]);
-    } else {
+      for (int i = 0; i < BPW; ++i) asm volatile("" : "+s"(vpg[i]));
+    };
+    auto issue_paged = [&](int j, uint8_t* buf, const uint16_t* base, const int* grp, const int* loff,
+                           const int* key, const int* colb, const int* pg, bool one_page, int row_bytes) {
+      const int kt0 = j * BN;
+      const int last = Lk - kt0 - 1;
+      const int glast = last >> 4;
 #pragma unroll
-      for (int i = 0; i < BPW; ++i)
-        dma16(vr, vb + (wave * BPW + i) * 1024, min(vkey[i], last) * vrow_bytes + vcol[i]);
-    }
-  };
+      for (int i = 0; i < BPW; ++i) {
+        const int geff = min(grp[i], glast);
+        const int page = pg[one_page ? 0 : i];  // scalar, loaded a step earlier
+        const uint8_t* gbase =
+            (const uint8_t*)base + (((int64_t)page << pshift) + ((kt0 + 16 * geff) & pmask)) * row_bytes;
+        const int vo = last >= BN - 1 ? loff[i] : (min(key[i], last) - 16 * geff) * row_bytes + colb[i];
+        dma16s(gbase, vo, buf + (wave * BPW + i) * 1024);
+      }
+    };
 
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m2 = kNegInf;  // reference max, base-2 units
-  float l = 0.f;
-  const float c2 = p.scale_log2;
-
-  // LDS read offsets
-  // K operand of k-step t, key block c: lane l reads chunk 2 t + l / 32 of key 32 c + l % 32,
-  // at kread[t % 2] + (2 c NQ + t / 2) 1024
-  constexpr int NQ = D / 32;
-  int kread[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int m = (lane >> 2) & 3;
-    kread[par] = ((lane >> 4) & 1) * NQ * 1024 + (lane & 15) * 64 + (2 * (par ^ (m >> 1)) + (half ^ (m & 1))) * 16;
-  }
-  const int vread = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-
-  // K operand of S^T = K Q^T for k-step t and key block c (16 bytes per lane)
-  auto kop = [&](const uint8_t* kb, int t, int c) -> u32x4 {
-    return *(const lds_u32x4*)(kb + kread[t & 1] + (2 * c * NQ + (t >> 1)) * 1024);
-  };
-  // V^T operand of O^T += V^T P^T for column block db and key group t4 (two transposing reads)
-  auto vop = [&](const uint8_t* vb, int db, int t4) -> bf16x8 {
-    const uint8_t* vp = vb + vread + db * VBLK + t4 * 1024;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  // Tail keys and (causal) keys above the diagonal -> -inf.  A key is admissible for
-  // this lane's query iff key <= klim; element (c, v) of the tile
-  // at kt0 holds key kt0 + 4 half + 32 c + 8 (v / 4) + v % 4, so the test is one compare
-  // of that compile-time offset with klim - kt0 - 4 half.
-  const int klim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;
-  auto mask1 = [&](int rel, float x, int c, int v) -> float {
-    return 32 * c + 8 * (v >> 2) + (v & 3) <= rel ? x : kNegInf;
-  };
-  auto finish_max = [&](float mx, float& mnew, bool& grow) {
-    mx = fmaxf(mx, xor32(mx)) * c2;
-    grow = mx > m2 + kRescaleSlack;  // also true on a row's first admissible key
-    mnew = grow ? mx : m2;
-  };
-
-  if (ntiles > 0) {
-    // prologue: K0, V0, K1 in flight; S_0 and its row max
-    if (PAGED) {
-      load_pages(0, kgrp, kpg, 1);
-      load_pages(0, vgrp, vpg, BPW);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      settle_pages();
-    }
-    issue_k(0, kbuf0);
-    issue_v(0, vbuf0);
-    if (ntiles > 1) {
+    auto issue_k = [&](int j, uint8_t* kb) {
       if (PAGED) {
-        load_pages(1, kgrp, kpg, 1);
+        issue_paged(j, kb, Kg, kgrp, kloff, kkey, kcol, kpg, true, krow_bytes);
+        return;
+      }
+      const int kt0 = j * BN;
+      const int last = Lk - kt0 - 1;  // last valid row of this tile (>= 0)
+      const int64_t krem = ((int64_t)last * ksn + D) * 2;  // bytes of valid keys from kt0 on
+      const u32x4s kr = buffer_rsrc(Kg + (int64_t)kt0 * ksn, krem);
+      if (last >= BN - 1) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) dma16(kr, kb + (wave * BPW + i) * 1024, kdoff[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+          dma16(kr, kb + (wave * BPW + i) * 1024, min(kkey[i], last) * krow_bytes + kcol[i]);
+      }
+    };
+    auto issue_v = [&](int j, uint8_t* vb) {
+      if (PAGED) {
+        issue_paged(j, vb, Vg, vgrp, vloff, vkey, vcol, vpg, false, vrow_bytes);
+        return;
+      }
+      const int kt0 = j * BN;
+      const int last = Lk - kt0 - 1;
+      const int64_t vrem = ((int64_t)last * vsn + D) * 2;
+      const u32x4s vr = buffer_rsrc(Vg + (int64_t)kt0 * vsn, vrem);
+      if (last >= BN - 1) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) dma16(vr, vb + (wave * BPW + i) * 1024, vdoff[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+          dma16(vr, vb + (wave * BPW + i) * 1024, min(vkey[i], last) * vrow_bytes + vcol[i]);
+      }
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    float m2 = kNegInf;  // reference max, base-2 units
+    float l = 0.f;
+    const float c2 = p.scale_log2;
+
+    // LDS read offsets
+    // K operand of k-step t, key block c: lane l reads chunk 2 t + l / 32 of key 32 c + l % 32,
+    // at kread[t % 2] + (2 c NQ + t / 2) 1024
+    constexpr int NQ = D / 32;
+    int kread[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int m = (lane >> 2) & 3;
+      kread[par] = ((lane >> 4) & 1) * NQ * 1024 + (lane & 15) * 64 + (2 * (par ^ (m >> 1)) + (half ^ (m & 1))) * 16;
+    }
+    const int vread = (4 * half + (lane & 15) / 4) * 64 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+    // K operand of S^T = K Q^T for k-step t and key block c (16 bytes per lane)
+    auto kop = [&](const uint8_t* kb, int t, int c) -> u32x4 {
+      return *(const lds_u32x4*)(kb + kread[t & 1] + (2 * c * NQ + (t >> 1)) * 1024);
+    };
+    // V^T operand of O^T += V^T P^T for column block db and key group t4 (two transposing reads)
+    auto vop = [&](const uint8_t* vb, int db, int t4) -> bf16x8 {
+      const uint8_t* vp = vb + vread + db * VBLK + t4 * 1024;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 512));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // Tail keys and (causal) keys above the diagonal -> -inf.  A key is admissible for
+    // this lane's query iff key <= klim; element (c, v) of the tile
+    // at kt0 holds key kt0 + 4 half + 32 c + 8 (v / 4) + v % 4, so the test is one compare
+    // of that compile-time offset with klim - kt0 - 4 half.
+    const int klim = CAUSAL ? min(Lk - 1, qi + shift) : Lk - 1;
+    auto mask1 = [&](int rel, float x, int c, int v) -> float {
+      return 32 * c + 8 * (v >> 2) + (v & 3) <= rel ? x : kNegInf;
+    };
+    auto finish_max = [&](float mx, float& mnew, bool& grow) {
+      mx = fmaxf(mx, xor32(mx)) * c2;
+      grow = mx > m2 + kRescaleSlack;  // also true on a row's first admissible key
+      mnew = grow ? mx : m2;
+    };
+
+    if (ntiles > 0) {
+      // prologue: K0, V0, K1 in flight; S_0 and its row max
+      if (PAGED) {
+        load_pages(0, kgrp, kpg, 1);
+        load_pages(0, vgrp, vpg, BPW);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         settle_pages();
       }
-      issue_k(1, kbuf1);
-    }
-    if (PAGED) {  // pages of the first step's loads: K_2 and V_1
-      if (ntiles > 2) load_pages(2, kgrp, kpg, 1);
-      if (ntiles > 1) load_pages(1, vgrp, vpg, BPW);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    f32x16 sA[NS], sB[NS];  // S of the current and the next tile, alternating roles
-#pragma unroll
-    for (int c = 0; c < NS; ++c) sA[c] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int c = 0; c < NS; ++c)
-        sA[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop(kbuf0, t, c)), qreg[t], sA[c], 0, 0, 0);
-    float mnew;
-    bool grow;
-    {
-      float mx = kNegInf;
-#pragma unroll
-      for (int c = 0; c < NS; ++c)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (nfull < 1) sA[c][v] = mask1(klim - 4 * half, sA[c][v], c, v);
-          mx = fmaxf(mx, sA[c][v]);
+      issue_k(0, kbuf0);
+      issue_v(0, vbuf0);
+      if (ntiles > 1) {
+        if (PAGED) {
+          load_pages(1, kgrp, kpg, 1);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          settle_pages();
         }
-      finish_max(mx, mnew, grow);
-    }
-
-    // Step j, software-pipelined inside one wavefront (MFMA and VALU work of the same
-    // wavefront overlap; separate wavefronts on a SIMD barely do):
-    //   phase 1: S_{j+1} = K_{j+1} Q^T (NS MFMAs per k-step) interleaved with the
-    //            exponentials, row sums and bf16 packing of tile j;
-    //   phase 2: O^T += V_j^T P_j^T (1 MFMA per chunk) interleaved with masking and the
-    //            row max of tile j+1.
-    // Scheduling barriers keep each chunk's MFMAs next to its VALU share.  Tiles that
-    // cross the diagonal or the sequence end are masked after phase 2 (a few per row
-    // block).  The last step's S_{j+1} is computed on a stale buffer and discarded.
-    // Step j: see the comment above.  Buffers: K_j in kbuf[j % 2], V_j in vbuf[j % 2].
-    auto step = [&](int j, const uint8_t* kcur, uint8_t* kdma, const uint8_t* vcur, uint8_t* vdma,
-                    f32x16* s_cur, f32x16* sn) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K_{j+1}, V_j landed
-      __syncthreads();                                   // ... and every wave's
-      if (PAGED) settle_pages();  // the page ids loaded with them too
-      // the first two k-steps' K operands are requested before anything else
-      constexpr int KPF = 2;  // k-steps of K operands in flight
-      u32x4 a[KPF][NS];
-#pragma unroll
-      for (int u = 0; u < KPF; ++u)
-#pragma unroll
-        for (int c = 0; c < NS; ++c) a[u][c] = kop(kcur, u, c);
-      if (j + 2 < ntiles) issue_k(j + 2, kdma);
-      if (j + 1 < ntiles) issue_v(j + 1, vdma);
-      if (PAGED) {  // pages of the next step's loads, landing with this step's tiles
-        if (j + 3 < ntiles) load_pages(j + 3, kgrp, kpg, 1);
-        if (j + 2 < ntiles) load_pages(j + 2, vgrp, vpg, BPW);
+        issue_k(1, kbuf1);
       }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {      // deferred rescale (rare)
-        const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-        m2 = mnew;
+      if (PAGED) {  // pages of the first step's loads: K_2 and V_1
+        if (ntiles > 2) load_pages(2, kgrp, kpg, 1);
+        if (ntiles > 1) load_pages(1, vgrp, vpg, BPW);
       }
-      const float muse = (m2 == kNegInf) ? 0.f : m2;  // no admissible key yet: p = 0
-
-      // phase 1
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      f32x16 sA[NS], sB[NS];  // S of the current and the next tile, alternating roles
 #pragma unroll
-      for (int c = 0; c < NS; ++c) sn[c] = f32x16{};
-      bf16x8 pb[NP];
-      // Row sum of P_j: with 64-key tiles at 2 wavefronts per SIMD the fp32 P values stay
-      // in registers and are summed in phase 2, whose VALU share is light (phase 1 carries
-      // the exponentials; measured +1 %); the 3-wavefront configuration has no registers
-      // to spare and sums in phase 1.
-      constexpr bool DEFER_SUM = WPE == 2;
-      // In that configuration the last MV elements of P_j are also computed in phase 2:
-      // its MFMAs then run key-group-major, so the last group's P operand is first needed
-      // at chunk (NP - 1) DB, after those elements (measured +0.7 %).
-      constexpr int MV = DEFER_SUM ? ((NP - 1) * DB < 4 ? (NP - 1) * DB : 4) : 0;
-      constexpr int P1 = 16 * NS - MV;  // elements of P_j computed in phase 1
-      float rs = 0.f;
-      float pvs[DEFER_SUM ? 16 * NS : 1];
+      for (int c = 0; c < NS; ++c) sA[c] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        u32x4 n[NS];
-#pragma unroll
-        for (int c = 0; c < NS; ++c) n[c] = (t + KPF < DT) ? kop(kcur, t + KPF, c) : a[t % KPF][c];
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int c = 0; c < NS; ++c)
-          sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[t % KPF][c]), qreg[t], sn[c], 0, 0, 0);
-        const int e0 = (t * P1) / DT, e1 = ((t + 1) * P1) / DT;
-#pragma unroll
-        for (int idx = e0; idx < e1; ++idx) {  // key group idx / 8, element idx % 8
-          const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
-          if constexpr (DEFER_SUM) pvs[idx] = pv;
-          else rs += pv;
-          pb[idx >> 3][idx & 7] = (__bf16)pv;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < NS; ++c) a[t % KPF][c] = n[c];
-      }
-      if constexpr (!DEFER_SUM) l += rs + xor32(rs);
-
-      // phase 2
-      constexpr int NCH = NP * DB;          // O^T MFMAs per tile
-      constexpr int SPC = 16 * NS / NCH;    // tile j+1 scores handled per chunk
-      const int kt1 = (j + 1) * BN;
-      float mx = kNegInf;
-      // V^T operands are read two MFMAs ahead: the transposing LDS reads take longer
-      // than one MFMA, and a one-ahead read made every MFMA of this phase wait for them
-      constexpr int VPF = 2;
-      bf16x8 vq[VPF];
-      // chunk k's (column block, key group): key-group-major when elements moved here
-      auto cdb = [](int k) { return MV ? k % DB : k / NP; };
-      auto ct4 = [](int k) { return MV ? k / DB : k % NP; };
-#pragma unroll
-      for (int u = 0; u < VPF; ++u) vq[u] = vop(vcur, cdb(u), ct4(u));
-#pragma unroll
-      for (int k = 0; k < NCH; ++k) {
-        const int db = cdb(k), t4 = ct4(k);
-        if (k < MV) {  // element P1 + k of P_j
-          const int idx = P1 + k;
-          const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
-          pvs[idx] = pv;
-          pb[idx >> 3][idx & 7] = (__bf16)pv;
-        }
-        const bf16x8 va = vq[k % VPF];
-        if (k + VPF < NCH) vq[k % VPF] = vop(vcur, cdb(k + VPF), ct4(k + VPF));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t4], oacc[db], 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < SPC; ++e) {
-          const int idx = k * SPC + e;
-          const int c = idx >> 4, v = idx & 15;
-          mx = fmaxf(mx, sn[c][v]);
-          if constexpr (DEFER_SUM) rs += pvs[idx];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (DEFER_SUM) l += rs + xor32(rs);
-      // a use of the row max here keeps its max3 chain between the MFMAs above; otherwise
-      // the compiler sinks it past them into the unmasked branch below
-      asm volatile("" : "+v"(mx));
-      if (j + 1 >= nfull) {  // tile j+1 crosses the diagonal or the tail: mask, redo the max
-        mx = kNegInf;
+          sA[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop(kbuf0, t, c)), qreg[t], sA[c], 0, 0, 0);
+      float mnew;
+      bool grow;
+      {
+        float mx = kNegInf;
 #pragma unroll
         for (int c = 0; c < NS; ++c)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            sn[c][v] = mask1(klim - kt1 - 4 * half, sn[c][v], c, v);
-            mx = fmaxf(mx, sn[c][v]);
+            if (nfull < 1) sA[c][v] = mask1(klim - 4 * half, sA[c][v], c, v);
+            mx = fmaxf(mx, sA[c][v]);
           }
+        finish_max(mx, mnew, grow);
       }
-      finish_max(mx, mnew, grow);
-    };
-    // unrolled by two so every buffer address is a compile-time offset and S alternates
-    // between sA and sB without copies; an odd last step runs after the loop
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-      step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
-      step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, sB, sA);
-    }
-    if (j < ntiles) step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
-  }
 
-  // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
-  if (qi < Lq) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    uint16_t* Og = (uint16_t*)p.o + ooff + (int64_t)qi * p.o_sn;
+      // Step j, software-pipelined inside one wavefront (MFMA and VALU work of the same
+      // wavefront overlap; separate wavefronts on a SIMD barely do):
+      //   phase 1: S_{j+1} = K_{j+1} Q^T (NS MFMAs per k-step) interleaved with the
+      //            exponentials, row sums and bf16 packing of tile j;
+      //   phase 2: O^T += V_j^T P_j^T (1 MFMA per chunk) interleaved with masking and the
+      //            row max of tile j+1.
+      // Scheduling barriers keep each chunk's MFMAs next to its VALU share.  Tiles that
+      // cross the diagonal or the sequence end are masked after phase 2 (a few per row
+      // block).  The last step's S_{j+1} is computed on a stale buffer and discarded.
+      // Step j: see the comment above.  Buffers: K_j in kbuf[j % 2], V_j in vbuf[j % 2].
+      auto step = [&](int j, const uint8_t* kcur, uint8_t* kdma, const uint8_t* vcur, uint8_t* vdma,
+                      f32x16* s_cur, f32x16* sn) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K_{j+1}, V_j landed
+        __syncthreads();                                   // ... and every wave's
+        if (PAGED) settle_pages();  // the page ids loaded with them too
+        // the first two k-steps' K operands are requested before anything else
+        constexpr int KPF = 2;  // k-steps of K operands in flight
+        u32x4 a[KPF][NS];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int u = 0; u < KPF; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __bf16 r0 = (__bf16)(oacc[db][4 * i + 0] * inv);
-        __bf16 r1 = (__bf16)(oacc[db][4 * i + 1] * inv);
-        __bf16 r2 = (__bf16)(oacc[db][4 * i + 2] * inv);
-        __bf16 r3 = (__bf16)(oacc[db][4 * i + 3] * inv);
-        const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
-        const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
-        *(u32x2*)(Og + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
+          for (int c = 0; c < NS; ++c) a[u][c] = kop(kcur, u, c);
+        if (j + 2 < ntiles) issue_k(j + 2, kdma);
+        if (j + 1 < ntiles) issue_v(j + 1, vdma);
+        if (PAGED) {  // pages of the next step's loads, landing with this step's tiles
+          if (j + 3 < ntiles) load_pages(j + 3, kgrp, kpg, 1);
+          if (j + 2 < ntiles) load_pages(j + 2, vgrp, vpg, BPW);
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {      // deferred rescale (rare)
+          const float alpha = exp2_fast(m2 - (mnew == kNegInf ? 0.f : mnew));
+          l *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+          m2 = mnew;
+        }
+        const float muse = (m2 == kNegInf) ? 0.f : m2;  // no admissible key yet: p = 0
+
+        // phase 1
+#pragma unroll
+        for (int c = 0; c < NS; ++c) sn[c] = f32x16{};
+        bf16x8 pb[NP];
+        // Row sum of P_j: with 64-key tiles at 2 wavefronts per SIMD the fp32 P values stay
+        // in registers and are summed in phase 2, whose VALU share is light (phase 1 carries
+        // the exponentials; measured +1 %); the 3-wavefront configuration has no registers
+        // to spare and sums in phase 1.
+        constexpr bool DEFER_SUM = WPE == 2;
+        // In that configuration the last MV elements of P_j are also computed in phase 2:
+        // its MFMAs then run key-group-major, so the last group's P operand is first needed
+        // at chunk (NP - 1) DB, after those elements (measured +0.7 %).
+        constexpr int MV = DEFER_SUM ? ((NP - 1) * DB < 4 ? (NP - 1) * DB : 4) : 0;
+        constexpr int P1 = 16 * NS - MV;  // elements of P_j computed in phase 1
+        float rs = 0.f;
+        float pvs[DEFER_SUM ? 16 * NS : 1];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          u32x4 n[NS];
+#pragma unroll
+          for (int c = 0; c < NS; ++c) n[c] = (t + KPF < DT) ? kop(kcur, t + KPF, c) : a[t % KPF][c];
+#pragma unroll
+          for (int c = 0; c < NS; ++c)
+            sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[t % KPF][c]), qreg[t], sn[c], 0, 0, 0);
+          const int e0 = (t * P1) / DT, e1 = ((t + 1) * P1) / DT;
+#pragma unroll
+          for (int idx = e0; idx < e1; ++idx) {  // key group idx / 8, element idx % 8
+            const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
+            if constexpr (DEFER_SUM) pvs[idx] = pv;
+            else rs += pv;
+            pb[idx >> 3][idx & 7] = (__bf16)pv;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int c = 0; c < NS; ++c) a[t % KPF][c] = n[c];
+        }
+        if constexpr (!DEFER_SUM) l += rs + xor32(rs);
+
+        // phase 2
+        constexpr int NCH = NP * DB;          // O^T MFMAs per tile
+        constexpr int SPC = 16 * NS / NCH;    // tile j+1 scores handled per chunk
+        const int kt1 = (j + 1) * BN;
+        float mx = kNegInf;
+        // V^T operands are read two MFMAs ahead: the transposing LDS reads take longer
+        // than one MFMA, and a one-ahead read made every MFMA of this phase wait for them
+        constexpr int VPF = 2;
+        bf16x8 vq[VPF];
+        // chunk k's (column block, key group): key-group-major when elements moved here
+        auto cdb = [](int k) { return MV ? k % DB : k / NP; };
+        auto ct4 = [](int k) { return MV ? k / DB : k % NP; };
+#pragma unroll
+        for (int u = 0; u < VPF; ++u) vq[u] = vop(vcur, cdb(u), ct4(u));
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+          const int db = cdb(k), t4 = ct4(k);
+          if (k < MV) {  // element P1 + k of P_j
+            const int idx = P1 + k;
+            const float pv = exp2_fast(__builtin_fmaf(s_cur[idx >> 4][idx & 15], c2, -muse));
+            pvs[idx] = pv;
+            pb[idx >> 3][idx & 7] = (__bf16)pv;
+          }
+          const bf16x8 va = vq[k % VPF];
+          if (k + VPF < NCH) vq[k % VPF] = vop(vcur, cdb(k + VPF), ct4(k + VPF));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t4], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < SPC; ++e) {
+            const int idx = k * SPC + e;
+            const int c = idx >> 4, v = idx & 15;
+            mx = fmaxf(mx, sn[c][v]);
+            if constexpr (DEFER_SUM) rs += pvs[idx];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (DEFER_SUM) l += rs + xor32(rs);
+        // a use of the row max here keeps its max3 chain between the MFMAs above; otherwise
+        // the compiler sinks it past them into the unmasked branch below
+        asm volatile("" : "+v"(mx));
+        if (j + 1 >= nfull) {  // tile j+1 crosses the diagonal or the tail: mask, redo the max
+          mx = kNegInf;
+#pragma unroll
+          for (int c = 0; c < NS; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              sn[c][v] = mask1(klim - kt1 - 4 * half, sn[c][v], c, v);
+              mx = fmaxf(mx, sn[c][v]);
+            }
+        }
+        finish_max(mx, mnew, grow);
+      };
+      // unrolled by two so every buffer address is a compile-time offset and S alternates
+      // between sA and sB without copies; an odd last step runs after the loop
+      int j = 0;
+      for (; j + 1 < ntiles; j += 2) {
+        step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
+        step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, sB, sA);
       }
-    if (p.lse != nullptr && half == 0)
-      p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+      if (j < ntiles) step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
+    }
+
+    // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
+    if (qi < Lq) {
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      uint16_t* Og = (uint16_t*)p.o + ooff + (int64_t)qi * p.o_sn;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __bf16 r0 = (__bf16)(oacc[db][4 * i + 0] * inv);
+          __bf16 r1 = (__bf16)(oacc[db][4 * i + 1] * inv);
+          __bf16 r2 = (__bf16)(oacc[db][4 * i + 2] * inv);
+          __bf16 r3 = (__bf16)(oacc[db][4 * i + 3] * inv);
+          const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
+          const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
+          *(u32x2*)(Og + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
+        }
+      if (p.lse != nullptr && half == 0)
+        p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+    }
+  };  // row_block
+
+  row_block(rbs[0]);
+  if (rbs[1] != rbs[0]) {
+    __syncthreads();  // every wave is done with the first block's LDS tiles
+    row_block(rbs[1]);
   }
 }
 
@@ -657,7 +709,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bf16_t(const FwdParams& p, hipStream_t s) {
   constexpr int NW = kFwdNW;
-  const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
+  // dense causal: one workgroup per pair of row blocks (block_coords_pair)
+  const int64_t nblk = (int64_t)(CAUSAL && !VARLEN ? (p.n_rb + 1) / 2 : p.n_rb) * p.H * p.B;
   if (nblk <= 0) return hipSuccess;
   const bool paged = VARLEN && p.block_table != nullptr;
   // causal varlen / paged batches of short sequences: 32-key tiles at 3 wavefronts per
