@@ -52,10 +52,28 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# The hardware-rate measurement (MFMA / VALU / LDS issue rates on one SIMD) behind the
+# forward kernel's roofline discussion: a separate executable, not part of the library.
+HW_RATES_SRC = "hw_rates.hip"
+HW_RATES = os.path.join(HERE, "hw_rates")
+
+
+def build_hw_rates(verbose: bool = False) -> str:
+    cmd = [hipcc(), *HIPFLAGS, os.path.join(CSRC, HW_RATES_SRC), "-o", HW_RATES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {HW_RATES_SRC} failed:\n{r.stdout}\n{r.stderr}")
+    return HW_RATES
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        hw = ex.submit(build_hw_rates, verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        hw.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

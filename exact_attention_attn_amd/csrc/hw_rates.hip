@@ -1,0 +1,135 @@
+// Hardware rates behind the forward kernel's roofline on gfx950: how fast one SIMD
+// issues 32x32x16 bf16 MFMAs alone, next to VALU work, and next to LDS operand reads of
+// the two sizes a wavefront tile can have (1 KiB per MFMA with 32 query rows per
+// wavefront, 512 B with 64).  A measurement aid, not part of libattn.so.
+//
+// Each test runs one workgroup per CU (the LDS array is sized above half of a CU's LDS)
+// of 4 or 8 wavefronts, i.e. 1 or 2 wavefronts per SIMD, and times its loop with the
+// shader's s_memtime counter ("ticks").  The MFMA pipe is full when the SIMD retires one
+// MFMA per kFullTicks ticks: the rate two wavefronts reach with nothing else to do.  The
+// operands are constant, so these are the chip's unthrottled rates.  Every LDS address
+// stays inside the workgroup's array; every store goes to one slot per wavefront.
+//
+// Build: hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops
+//        hw_rates.hip -o hw_rates        (build.py does this)
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <vector>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kIters = 256;
+constexpr int kLdsBytes = 81920;  // > 80 KiB: one workgroup per CU
+constexpr int kBlocks = 256;      // one per CU
+
+// Per iteration: 16 MFMAs over CH accumulator chains; RD LDS reads of 16 B per lane
+// (1 KiB per wavefront each) issued ahead of them; NV VALU instructions after each MFMA
+// (FMA and exp2, two to one, on 8 independent chains).
+template <int CH, int RD, int NV>
+__global__ void __launch_bounds__(512) mix(long long* ticks, float* sink, float a, float b) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid * 16; i < 65536; i += blockDim.x * 16) *(u32x4*)(sm + i) = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  f32x16 c[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) c[i] = f32x16{};
+  bf16x8 A, B;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    A[i] = (__bf16)(0.5f + i * 0.01f);
+    B[i] = (__bf16)(0.25f - i * 0.01f);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = a + 0.01f * lane + 0.1f * i;
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
+  const unsigned off = (unsigned)(wave * 4096 + lane * 16);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const long long t0 = clock64();
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 r[RD > 0 ? RD : 1];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) r[i] = *(const lds_u32x4*)(base + ((off + ((it * 7 + i) & 15) * 1024) & 0xFFF0u));
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      c[m % CH] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, c[m % CH], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int i = (m * NV + v) & 7;
+        if (v % 3 == 1) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+        else x[i] = __builtin_fmaf(x[i], a, b);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < RD; ++i) acc ^= r[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const long long t1 = clock64();
+  float s = (float)(acc.x + acc.y + acc.z + acc.w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  if (s == 1234.5f) sink[tid] = s;  // keeps the work; never true
+  if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
+}
+
+constexpr double kFullTicks = 24.0;  // measured below: two wavefronts, MFMA only
+
+template <int CH, int RD, int NV>
+double run(int waves_per_simd, long long* ticks, float* sink, const char* what, bool print = true) {
+  const int threads = 256 * waves_per_simd;
+  double per = 0.0;
+  for (int rep = 0; rep < 3; ++rep) {
+    hipLaunchKernelGGL((mix<CH, RD, NV>), dim3(kBlocks), dim3(threads), 0, 0, ticks, sink, 0.3f, 0.7f);
+    if (hipDeviceSynchronize() != hipSuccess) {
+      fprintf(stderr, "launch failed\n");
+      return -1.0;
+    }
+    std::vector<long long> h(kBlocks * 8);
+    if (hipMemcpy(h.data(), ticks, h.size() * sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess) return -1.0;
+    double s = 0.0;
+    int n = 0;
+    for (int b = 0; b < kBlocks; ++b)
+      for (int w = 0; w < threads / 64; ++w) {
+        s += (double)h[b * 8 + w];
+        ++n;
+      }
+    per = s / n / kIters / 16.0;  // ticks per MFMA per wavefront (last repetition)
+  }
+  const double pipe = kFullTicks * waves_per_simd / per;
+  const double lds = RD * 1024.0 * 4 * waves_per_simd / (per * 16.0);  // LDS bytes per tick per CU
+  if (print)
+    printf("| %-58s | %d | %6.1f | %5.1f %% | %6.1f |\n", what, waves_per_simd, per, 100.0 * pipe, lds);
+  return per;
+}
+
+}  // namespace
+
+int main() {
+  long long* ticks = nullptr;
+  float* sink = nullptr;
+  if (hipMalloc(&ticks, kBlocks * 8 * sizeof(long long)) != hipSuccess) return 1;
+  if (hipMalloc(&sink, 512 * sizeof(float)) != hipSuccess) return 1;
+  printf("| loop (per MFMA: LDS bytes read / VALU instructions) | wavefronts per SIMD | ticks per MFMA per wavefront | MFMA pipe busy | LDS B/tick/CU |\n");
+  printf("|---|---|---|---|---|\n");
+  run<4, 0, 0>(2, ticks, sink, "MFMA only, 4 chains per wavefront");
+  run<8, 0, 0>(1, ticks, sink, "MFMA only, 8 chains");
+  run<8, 0, 4>(1, ticks, sink, "MFMA + 4 VALU, 8 chains");
+  run<4, 16, 0>(2, ticks, sink, "MFMA + 1 KiB LDS");
+  run<4, 16, 5>(2, ticks, sink, "MFMA + 1 KiB LDS + 5 VALU (32 rows per wavefront)");
+  run<4, 8, 0>(2, ticks, sink, "MFMA + 512 B LDS");
+  run<4, 8, 5>(2, ticks, sink, "MFMA + 512 B LDS + 5 VALU (64 rows, if it fit 2/SIMD)");
+  run<8, 8, 4>(1, ticks, sink, "MFMA + 512 B LDS + 4 VALU, 8 chains (64 rows per wavefront)");
+  return 0;
+}
