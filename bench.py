@@ -205,6 +205,9 @@ def main() -> int:
                                        "prefill_paged", "bwd", "bwd_varlen"],
                     default=None,
                     help="time one entry point only (profiling aid); the JSON line is still printed")
+    ap.add_argument("--gqa-batch", type=int, default=64,
+                    help="sequences of the grouped-query decode leg (64: the workload of the JSON line; more: "
+                         "the same length distribution on a larger batch, to separate launch ramp from steady state)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -276,14 +279,15 @@ def main() -> int:
         log(f"[bench] decode workload ready ({time.perf_counter() - t:.1f} s)")
 
     if "decode_gqa" in need:
-        w6 = synth.workload("gqa_decode")
+        w6 = synth.workload("gqa_decode") if args.gqa_batch == 64 else \
+            synth.paged(args.gqa_batch, 16, 128, 512, 8192, 16, seed=0, H_kv=8)
         q6, kc6, vc6 = dev(w6.q), dev(w6.k_cache), dev(w6.v_cache)
         bt6, cl6 = dev(w6.block_table), dev(w6.context_lens)
         maxctx6 = int(w6.context_lens.max())
-        ws6 = torch.empty(attn.attn_decode_paged_workspace_size(64, 16, 128, maxctx6, 16), dtype=torch.uint8,
+        ws6 = torch.empty(attn.attn_decode_paged_workspace_size(w6.B, 16, 128, maxctx6, 16), dtype=torch.uint8,
                           device="cuda")
         o6 = torch.empty_like(q6)
-        l6 = torch.empty((64, 16), dtype=torch.float32, device="cuda")
+        l6 = torch.empty((w6.B, 16), dtype=torch.float32, device="cuda")
         w6.k_cache = w6.v_cache = None
         log(f"[bench] grouped-query decode workload ready ({time.perf_counter() - t:.1f} s)")
 
@@ -439,8 +443,8 @@ def main() -> int:
                              bytes_per_launch=by5, note="split kernel + combine kernel, both inside the timed launch",
                              **rate("decode", by5, "GB/s", PEAK_HBM_GBS))
     if "decode_gqa" in ms:
-        by6 = decode_bytes(w6.context_lens, 64, 16, 128, 16, H_kv=8)
-        res["decode_gqa"] = dict(workload="64 seqs ctx U[512,8192] (seed 0) 16-token pages H=16 H_kv=8 d=128 bf16",
+        by6 = decode_bytes(w6.context_lens, w6.B, 16, 128, 16, H_kv=8)
+        res["decode_gqa"] = dict(workload=f"{w6.B} seqs ctx U[512,8192] (seed 0) 16-token pages H=16 H_kv=8 d=128 bf16",
                                  bytes_per_launch=by6, note="KV bytes counted once per KV head (grouped-query)",
                                  **rate("decode_gqa", by6, "GB/s", PEAK_HBM_GBS))
     if "bwd" in ms:

@@ -1,7 +1,8 @@
 // Hardware rates behind the forward kernel's roofline on gfx950: how fast one SIMD
 // issues 32x32x16 bf16 MFMAs alone, next to VALU work, and next to LDS operand reads of
 // the two sizes a wavefront tile can have (1 KiB per MFMA with 32 query rows per
-// wavefront, 512 B with 64).  A measurement aid, not part of libattn.so.
+// wavefront, 512 B with 64); and the same for 16x16x32 MFMAs whose LDS operand serves 2-4
+// query blocks of 16 rows.  A measurement aid, not part of libattn.so.
 //
 // Each test runs one workgroup per CU (the LDS array is sized above half of a CU's LDS)
 // of 4 or 8 wavefronts, i.e. 1 or 2 wavefronts per SIMD, and times its loop with the
@@ -84,6 +85,60 @@ __global__ void __launch_bounds__(512) mix(long long* ticks, float* sink, float 
   if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
 }
 
+// The same with v_mfma_f32_16x16x32_bf16 (half the flops of a 32x32x16): NA LDS reads of
+// 1 KiB per iteration, each the A operand of R MFMAs (R query blocks of 16 rows sharing
+// it), NV VALU instructions after each MFMA.
+template <int NA, int R, int NV>
+__global__ void __launch_bounds__(512) mix16(long long* ticks, float* sink, float a, float b) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[kLdsBytes];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid * 16; i < 65536; i += blockDim.x * 16) *(u32x4*)(sm + i) = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  f32x4 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4{};
+  bf16x8 B[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) B[r][i] = (__bf16)(0.25f - i * 0.01f + r);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = a + 0.01f * lane + 0.1f * i;
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
+  const unsigned off = (unsigned)(wave * 4096 + lane * 16);
+  const long long t0 = clock64();
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 nxt = *(const lds_u32x4*)(base + ((off + ((it * 7) & 15) * 1024) & 0xFFF0u));
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const u32x4 cur = nxt;
+      if (i + 1 < NA) nxt = *(const lds_u32x4*)(base + ((off + ((it * 7 + i + 1) & 15) * 1024) & 0xFFF0u));
+      const bf16x8 A = __builtin_bit_cast(bf16x8, cur);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int ci = (i * R + r) & 7;
+        c[ci] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[r], c[ci], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int j = (r * NV + v) & 7;
+          if (v % 3 == 1) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+          else x[j] = __builtin_fmaf(x[j], a, b);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const long long t1 = clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i] + c[i][0] + c[i][1] + c[i][2] + c[i][3];
+  if (s == 1234.5f) sink[tid] = s;
+  if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
+}
+
 constexpr double kFullTicks = 24.0;  // measured below: two wavefronts, MFMA only
 
 template <int CH, int RD, int NV>
@@ -116,6 +171,23 @@ double run(int waves_per_simd, long long* ticks, float* sink, const char* what, 
 
 }  // namespace
 
+// 16x16x32 loops at two wavefronts per SIMD, reported per 32 Kflop (one 32x32x16's work).
+template <int NA, int R, int NV>
+void run16(long long* ticks, float* sink, const char* what) {
+  double per = 0.0;
+  for (int rep = 0; rep < 3; ++rep) {
+    hipLaunchKernelGGL((mix16<NA, R, NV>), dim3(kBlocks), dim3(512), 0, 0, ticks, sink, 0.3f, 0.7f);
+    if (hipDeviceSynchronize() != hipSuccess) return;
+    std::vector<long long> h(kBlocks * 8);
+    if (hipMemcpy(h.data(), ticks, h.size() * sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess) return;
+    double s = 0.0;
+    for (long long v : h) s += (double)v;
+    per = s / h.size() / kIters / (NA * R / 2.0);  // ticks per 32 Kflop per wavefront
+  }
+  const double lds = 1024.0 * NA * 8 / (per * NA * R / 2.0);
+  printf("| %-58s | 2 | %6.1f | %5.1f %% | %6.1f |\n", what, per, 100.0 * kFullTicks * 2 / per, lds);
+}
+
 int main() {
   long long* ticks = nullptr;
   float* sink = nullptr;
@@ -131,5 +203,12 @@ int main() {
   run<4, 8, 0>(2, ticks, sink, "MFMA + 512 B LDS");
   run<4, 8, 5>(2, ticks, sink, "MFMA + 512 B LDS + 5 VALU (64 rows, if it fit 2/SIMD)");
   run<8, 8, 4>(1, ticks, sink, "MFMA + 512 B LDS + 4 VALU, 8 chains (64 rows per wavefront)");
+  printf("\n16x16x32 MFMAs, per 32 Kflop (two of them), LDS A operand shared by R MFMAs:\n\n");
+  printf("| loop | wavefronts per SIMD | ticks per 32 Kflop per wavefront | MFMA pipe busy | LDS B/tick/CU |\n");
+  printf("|---|---|---|---|---|\n");
+  run16<8, 2, 0>(ticks, sink, "R = 2 (1 KiB LDS per 32 Kflop)");
+  run16<6, 3, 0>(ticks, sink, "R = 3 (1 KiB per 48 Kflop, 48 rows per wavefront)");
+  run16<6, 3, 3>(ticks, sink, "R = 3, 3 VALU per 16x16x32 (6 per 32 Kflop)");
+  run16<4, 4, 3>(ticks, sink, "R = 4 (1 KiB per 64 Kflop), 3 VALU per 16x16x32");
   return 0;
 }
