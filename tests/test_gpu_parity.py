@@ -335,6 +335,27 @@ def test_decode_long_context(A, H, H_kv):
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
+def test_decode_context_above_max_is_truncated(A):
+    """A context length above max_context_len (a caller error) is truncated to
+    max_context_len, in the split kernels and in the combine.  The block table and the
+    workspace are sized for the full lengths, so even without the truncation every read
+    would stay inside them (it would only give a different result)."""
+    import torch
+    ctx = [100, 5000, 777, 2048]
+    maxc = 1000
+    w = synth.paged(H=4, d=128, ctx=ctx, page=16, seed=99, H_kv=2)
+    ws = torch.empty(10 * A.attn_decode_paged_workspace_size(4, 4, 128, 5000, 16), dtype=torch.uint8, device="cuda")
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), maxc, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    clamped = np.minimum(w.context_lens, maxc).astype(np.int32)
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, clamped, w.scale)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
 def test_decode_identity_table_equals_dense_last_row(A):
     """Paged decode with pages in order == the last row of a causal dense run."""
     import torch
