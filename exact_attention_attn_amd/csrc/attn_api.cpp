@@ -333,6 +333,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
   p.rows = (int64_t)total_q * H;
   p.B = num_seqs; p.H = H; p.H_kv = H_kv; p.N = max_seqlen_q; p.Nk = max_seqlen_k;
+  p.total_q = total_q; p.total_k = total_k;
   p.kv_group = H / H_kv;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;

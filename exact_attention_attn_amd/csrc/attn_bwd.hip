@@ -27,6 +27,7 @@
 // direct-to-LDS loads into one swizzled layout per tensor that serves both the 16-byte
 // operand reads and the ds_read_b64_tr_b16 transposing reads without bank conflicts.
 #include "attn_internal.h"
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -83,22 +84,6 @@ __device__ __forceinline__ bf16x8 op_read(unsigned base, int t) {
 
 // Accumulator element v of lane (half = lane / 32) sits in row 8 (v / 4) + 4 half + v % 4.
 __device__ __forceinline__ int acc_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
-
-// 32x32 accumulator -> 16 rows of one column, written as bf16 rows of a row-major
-// tensor: lane's column is the output row, accumulator rows are output columns.
-template <int DB>
-__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, float mul, int half) {
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 r0 = (__bf16)(acc[db][4 * i + 0] * mul), r1 = (__bf16)(acc[db][4 * i + 1] * mul);
-      const __bf16 r2 = (__bf16)(acc[db][4 * i + 2] * mul), r3 = (__bf16)(acc[db][4 * i + 3] * mul);
-      const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
-      const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
-      *(u32x2*)(dst + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
-    }
-}
 
 // acc += A B on an AGPR-pinned accumulator (the dK / dV accumulators: the dK/dV kernel
 // needs more than 256 registers).  The hazard recognizer does not see inside inline
@@ -198,6 +183,68 @@ struct TilePairDma {
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+// The 32 rows held by a wavefront's 32x32 accumulators (lane l: row l % 32; DB
+// accumulators of 32 columns each) -> bf16 rows [0, nrows) of a row-major tensor at dst0
+// (row stride in elements), through the wavefront's own LDS slice of 64 D bytes: written
+// in the accumulators' layout with the 16-byte chunk index XOR-swizzled by the row
+// (conflict-free), read back as whole rows, and stored 16 bytes per lane, so that each
+// store instruction writes 64 / (D / 8) complete rows instead of 16 bytes of 32 rows.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(unsigned slice, uint16_t* dst0, int64_t stride, int nrows,
+                                               const f32x16* acc, float mul, int lane) {
+  constexpr int DB = D / 32, CPR = D / 8, RB = D * 2, RPI = 64 / CPR;
+  const int half = lane >> 5, row = lane & 31;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 r0 = (__bf16)(acc[db][4 * i + 0] * mul), r1 = (__bf16)(acc[db][4 * i + 1] * mul);
+      const __bf16 r2 = (__bf16)(acc[db][4 * i + 2] * mul), r3 = (__bf16)(acc[db][4 * i + 3] * mul);
+      const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
+      const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
+      const int c = 4 * db + i;  // chunk of columns 32 db + 8 i .. +7; this lane's half is 4 of them
+      *(lds_u32x2*)lds_at(slice + (unsigned)(row * RB + ((c ^ (row % CPR)) * 16) + 8 * half)) = u32x2{u0, u1};
+    }
+#pragma unroll
+  for (int n = 0; n < 32 / RPI; ++n) {
+    const int r = n * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *(const lds_u32x4*)lds_at(slice + (unsigned)(r * RB + ((c ^ (r % CPR)) * 16)));
+    if (r < nrows) *(u32x4*)(dst0 + (int64_t)r * stride + c * 8) = v;
+  }
+}
+
+// Variable-length launches in compact form: the batch's blocks of 128 rows (or keys),
+// sequence by sequence, are numbered without gaps; block u -> sequence s (-1 past the
+// last block), its block index blk and its row ranges [q0, q1) and [k0, k1) in the packed
+// tensors.  scan_q: the blocks are row blocks (else key blocks).  Lane i reads sequence
+// i's bounds (B <= 64), the wavefront takes an inclusive prefix sum of the block counts,
+// and the first lane whose sum exceeds u holds the block: one round of loads and
+// register work, instead of a walk over the sequences.
+__device__ __forceinline__ void seq_block(const BwdParams& p, bool scan_q, int u, int lane, int& s, int& blk,
+                                          int& q0, int& q1, int& k0, int& k1) {
+  const int i = min(lane, p.B - 1);
+  const int qa = p.cu_q[i], qe = p.cu_q[i + 1], ka = p.cu_k[i], ke = p.cu_k[i + 1];
+  const int n = lane < p.B ? ((scan_q ? qe - qa : ke - ka) + 127) >> 7 : 0;
+  int incl = n;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(incl > u);
+  s = -1;
+  blk = q0 = q1 = k0 = k1 = 0;
+  if (m == 0) return;
+  s = (int)__builtin_ctzll(m);
+  blk = u - __builtin_amdgcn_readlane(incl - n, s);
+  q0 = __builtin_amdgcn_readlane(qa, s);
+  q1 = __builtin_amdgcn_readlane(qe, s);
+  k0 = __builtin_amdgcn_readlane(ka, s);
+  k1 = __builtin_amdgcn_readlane(ke, s);
+}
+
 // Extents and offsets of (sequence b, query head h, KV head hk).  Dense tensors are
 // [B, H, N, d] / [B, H_kv, Nk, d]; variable-length ones are token-major [total, H, d] /
 // [total, H_kv, d] with sequence b's rows from cu_q[b] / cu_k[b] (the forward's varlen
@@ -212,11 +259,14 @@ struct BwdGeo {
   int64_t r0;      // lse / workspace index of query row 0 of head h
   int rrs;         // ... its stride between rows
   int64_t rhs;     // ... and between consecutive query heads
-  __device__ BwdGeo(const BwdParams& p, int b, int h, int hk) {
+  __device__ BwdGeo(const BwdParams& p, int b, int h, int hk)
+      : BwdGeo(p, h, hk, VARLEN ? p.cu_q[b] : 0, VARLEN ? p.cu_q[b + 1] : 0, VARLEN ? p.cu_k[b] : 0,
+               VARLEN ? p.cu_k[b + 1] : 0, b) {}
+  // varlen: the sequence's rows [qs, qe) and keys [ks, ke) given; dense: batch b
+  __device__ BwdGeo(const BwdParams& p, int h, int hk, int qs, int qe, int ks, int ke, int b) {
     if (VARLEN) {
-      const int qs = p.cu_q[b], ks = p.cu_k[b];
-      Lq = p.cu_q[b + 1] - qs;
-      Lk = p.cu_k[b + 1] - ks;
+      Lq = qe - qs;
+      Lk = ke - ks;
       q0 = ((int64_t)qs * p.H + h) * D;
       k0 = ((int64_t)ks * p.H_kv + hk) * D;
       qrs = p.H * D;
@@ -283,8 +333,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_rb = (p.N + BM - 1) / BM;  // p.N: the longest sequence's rows (varlen)
-  int b, h, rbi;
-  {
+  int b, h, rb;
+  int sq0 = 0, sq1 = 0, sk0 = 0, sk1 = 0;  // compact grid: the sequence's row and key ranges
+  const bool compact = VARLEN && p.units_q > 0;
+  if (compact) {
+    // compact varlen grid (seq_block): units_q blocks per query head; XCD x takes KV
+    // heads x, x + 8, ... (when H_kv is a multiple of 8), each with every query head of
+    // its group back to back, each with its blocks in sequence order
+    const int G = p.kv_group, nu = p.units_q;
+    const int bid = blockIdx.x;
+    int u;
+    if ((p.H_kv & 7) == 0) {
+      const int x = bid & 7, i = bid >> 3;
+      const int per = G * nu;
+      const int hk = x + 8 * (i / per);
+      const int r = i - (i / per) * per;
+      const int member = r / nu;
+      u = r - member * nu;
+      h = hk * G + member;
+    } else {
+      h = bid % p.H;
+      u = bid / p.H;
+    }
+    int rbi;
+    seq_block(p, true, u, lane, b, rbi, sq0, sq1, sk0, sk1);
+    if (b < 0) return;  // past the batch's last block; no barrier passed yet
+    rb = CAUSAL ? ((sq1 - sq0 + 127) >> 7) - 1 - rbi : rbi;  // heaviest row block of the sequence first
+  } else {
+    int rbi;
     // Workgroups go round-robin to the 8 XCDs (blockIdx % 8), each with its own L2.  For
     // variable-length batches (many (sequence, KV head) pairs), when the pairs are a
     // multiple of 8, XCD x takes pairs x, x + 8, ... one after the other, and for each
@@ -309,10 +385,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       b = pair / p.H;
       h = pair - b * p.H;
     }
+    rb = CAUSAL ? n_rb - 1 - rbi : rbi;  // heaviest row block first
   }
-  const int rb = CAUSAL ? n_rb - 1 - rbi : rbi;  // heaviest row block first
   const int hk = h / p.kv_group;
-  const BwdGeo<D, VARLEN> geo(p, b, h, hk);
+  const BwdGeo<D, VARLEN> geo = compact ? BwdGeo<D, VARLEN>(p, h, hk, sq0, sq1, sk0, sk1, b) : BwdGeo<D, VARLEN>(p, b, h, hk);
   const int Lq = geo.Lq, Lk = geo.Lk, shift = Lk - Lq;
   const int row0 = rb * BM;
   if (row0 >= Lq) return;  // uniform over the workgroup; no barrier passed yet
@@ -429,7 +505,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int t4 = 0; t4 < 2; ++t4)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db][t4], dsb[t4], acc[db], 0, 0, 0);
   }
-  if (qi < Lq) store_rows<DB>((uint16_t*)p.dq + geo.q0 + (int64_t)qi * geo.qrs, acc, p.scale, half);
+  __syncthreads();  // every wave is done with the last K / V stage: the LDS stages dQ
+  const int wrow0 = row0 + wave * 32;
+  store_rows_lds<D>(lsm + (unsigned)(wave * 32 * D * 2), (uint16_t*)p.dq + geo.q0 + (int64_t)wrow0 * geo.qrs,
+                    geo.qrs, Lq - wrow0, acc, p.scale, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -455,8 +534,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkb = (p.Nk + BK - 1) / BK;  // p.Nk: the longest sequence's keys (varlen)
-  int pair, kb;  // (sequence, KV head) and key block; low (heaviest causal) key blocks first
-  {
+  int b, hk, kb;  // sequence, KV head and key block; low (heaviest causal) key blocks first
+  int sq0 = 0, sq1 = 0, sk0 = 0, sk1 = 0;  // compact grid: the sequence's row and key ranges
+  const bool compact = VARLEN && p.units_k > 0;
+  if (compact) {
+    // compact varlen grid (seq_block): units_k key blocks per KV head; XCD x takes KV
+    // heads x, x + 8, ... (when H_kv is a multiple of 8), each with its blocks in sequence
+    // order, so a sequence's blocks run side by side and share its query-side tiles in L2
+    const int nu = p.units_k;
+    const int bid = blockIdx.x;
+    int u;
+    if ((p.H_kv & 7) == 0) {
+      const int x = bid & 7, i = bid >> 3;
+      hk = x + 8 * (i / nu);
+      u = i - (i / nu) * nu;
+    } else {
+      hk = bid % p.H_kv;
+      u = bid / p.H_kv;
+    }
+    seq_block(p, false, u, lane, b, kb, sq0, sq1, sk0, sk1);
+    if (b < 0) return;  // past the batch's last block; no barrier passed yet
+  } else {
+    int pair;
     // As in the dQ kernel, for variable-length batches: XCD x takes pairs x, x + 8, ...
     // one after the other with all their key blocks, so the pair's query-side tiles stay
     // in that XCD's L2 (measured: varlen dK/dV -7 %; the dense batch unchanged).
@@ -470,10 +569,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       pair = bid % npairs;
       kb = bid / npairs;
     }
+    b = pair / p.H_kv;
+    hk = pair - b * p.H_kv;
   }
-  const int b = pair / p.H_kv, hk = pair - b * p.H_kv;
   const int G = p.kv_group;
-  const BwdGeo<D, VARLEN> geo(p, b, hk * G, hk);  // query head: the group's first
+  // query head: the group's first
+  const BwdGeo<D, VARLEN> geo =
+      compact ? BwdGeo<D, VARLEN>(p, hk * G, hk, sq0, sq1, sk0, sk1, b) : BwdGeo<D, VARLEN>(p, b, hk * G, hk);
   const int Lq = geo.Lq, Lk = geo.Lk, shift = Lk - Lq;
   const int k0 = kb * BK;
   if (k0 >= Lk) return;  // uniform over the workgroup; no barrier passed yet
@@ -702,31 +804,49 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   if (st < nsteps) step(st, sA, dA, sB, dB, true);
   agpr_settle();
-  if (key < Lk) {
-    const int64_t row = geo.k0 + (int64_t)key * geo.krs;
-    store_rows<DB>((uint16_t*)p.dk + row, dk, p.scale, half);
-    store_rows<DB>((uint16_t*)p.dv + row, dv, 1.0f, half);
+  __syncthreads();  // every wave is done with the ring: the LDS stages dK and dV
+  {
+    const int wk0 = k0 + wave * 32;
+    const int64_t row = geo.k0 + (int64_t)wk0 * geo.krs;
+    const unsigned slice = lsm + (unsigned)(wave * 2 * 32 * D * 2);
+    store_rows_lds<D>(slice, (uint16_t*)p.dk + row, geo.krs, Lk - wk0, dk, p.scale, lane);
+    store_rows_lds<D>(slice + 32 * D * 2, (uint16_t*)p.dv + row, geo.krs, Lk - wk0, dv, 1.0f, lane);
   }
 }
+
+// Variable-length batches of at most kCompactSeqs sequences launch compact grids
+// (seq_block): an upper bound of the batch's 128-row (key) blocks per head, from the
+// packed row counts (sum over s of ceil(L_s / 128) <= (total + 127 B) / 128), instead of
+// ceil(max_seqlen / 128) blocks for every sequence.  At one dK/dV workgroup per CU,
+// each of the empty workgroups of the plain grid held a CU for its launch, its
+// parameter and cu_seqlens reads and its exit (a per-workgroup timeline showed 5-6 us
+// between a CU's consecutive real workgroups against 1 us in the dense case).
+constexpr int kCompactSeqs = 64;  // seq_block: one sequence per lane
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   // p.N, p.Nk: rows and keys per sequence (dense) or of the longest sequence (varlen)
+  BwdParams q = p;
+  q.units_q = q.units_k = 0;
+  if (VARLEN && p.B <= kCompactSeqs) {
+    q.units_q = (int)std::min<int64_t>((int64_t)p.B * ((p.N + 127) / 128), ((int64_t)p.total_q + 127 * (int64_t)p.B) / 128);
+    q.units_k = (int)std::min<int64_t>((int64_t)p.B * ((p.Nk + 127) / 128), ((int64_t)p.total_k + 127 * (int64_t)p.B) / 128);
+  }
   if (p.rows > 0) {
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((p.rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((p.rows + RPB - 1) / RPB)), dim3(256), 0, s, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nq = (int64_t)((p.N + 127) / 128) * p.B * p.H;
+    const int64_t nq = (VARLEN && q.units_q > 0 ? (int64_t)q.units_q : (int64_t)((p.N + 127) / 128) * p.B) * p.H;
     if (nq > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nq), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nq), dim3(256), 0, s, q);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  const int64_t nk = (int64_t)((p.Nk + 127) / 128) * p.B * p.H_kv;
+  const int64_t nk = (VARLEN && q.units_k > 0 ? (int64_t)q.units_k : (int64_t)((p.Nk + 127) / 128) * p.B) * p.H_kv;
   if (nk > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nk), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)nk), dim3(256), 0, s, q);
     return hipGetLastError();
   }
   return hipSuccess;

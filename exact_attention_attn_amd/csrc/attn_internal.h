@@ -90,6 +90,8 @@ struct BwdParams {
   int64_t rows;       // query rows x heads: B H N, or total_q H
   int B, H, H_kv;
   int N, Nk;          // rows / keys per sequence; varlen: of the longest sequence
+  int total_q, total_k;  // varlen: rows of the packed query-side / key-side tensors
+  int units_q, units_k;  // varlen compact grids: blocks per head (0: one per max_seqlen block; set by the launcher)
   int kv_group;       // H / H_kv
   float scale;
   float scale_log2;
