@@ -139,6 +139,68 @@ __global__ void __launch_bounds__(512) mix16(long long* ticks, float* sink, floa
   if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
 }
 
+// The same loop with GL of the 1 KiB operand reads per iteration taken from global
+// memory (a 64 KiB buffer, L1/L2 resident) into registers instead of from LDS, one
+// iteration ahead (consumed, like the LDS reads, by an XOR into a sink).  PAT 0: the
+// MFMA operand pattern (lane l: row l % 32, 32 bytes of each of 32 rows of 256 B); PAT 1:
+// whole rows (lane l: row l / 16, 16 bytes; 4 complete rows per instruction).
+template <int RD, int GL, int PAT>
+__global__ void __launch_bounds__(512) mixg(long long* ticks, float* sink, const u32x4* __restrict__ gbuf) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid * 16; i < 65536; i += blockDim.x * 16) *(u32x4*)(sm + i) = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = f32x16{};
+  bf16x8 A, B;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    A[i] = (__bf16)(0.5f + i * 0.01f);
+    B[i] = (__bf16)(0.25f - i * 0.01f);
+  }
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
+  const unsigned off = (unsigned)(wave * 4096 + lane * 16);
+  // byte offset of this lane's 16 bytes in a 1 KiB operand block (a 4 KiB stretch of rows)
+  const unsigned goff = PAT == 0 ? (unsigned)((lane & 31) * 256 + (lane >> 5) * 16) : (unsigned)((lane >> 4) * 256 + (lane & 15) * 16);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 g[GL > 0 ? GL : 1];
+#pragma unroll
+  for (int i = 0; i < GL; ++i) g[i] = gbuf[(goff + i * 32u) / 16];
+  const long long t0 = clock64();
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 r[RD > 0 ? RD : 1], gn[GL > 0 ? GL : 1];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) r[i] = *(const lds_u32x4*)(base + ((off + ((it * 7 + i) & 15) * 1024) & 0xFFF0u));
+    const unsigned blk = (unsigned)(((it + 1) * 5) & 15) * 4096u;  // 4 KiB stretch in the 64 KiB buffer
+#pragma unroll
+    for (int i = 0; i < GL; ++i) gn[i] = gbuf[(blk + goff + (unsigned)(i % 8) * 32u + (unsigned)(i / 8) * 8192u) % 65536u / 16u];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      c[m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, c[m % 4], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < RD; ++i) acc ^= r[i];
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      acc ^= g[i];
+      g[i] = gn[i];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const long long t1 = clock64();
+  float s = (float)(acc.x + acc.y + acc.z + acc.w);
+#pragma unroll
+  for (int i = 0; i < GL; ++i) s += (float)(g[i].x ^ g[i].w);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  if (s == 1234.5f) sink[tid] = s;  // keeps the work; never true
+  if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
+}
+
 constexpr double kFullTicks = 24.0;  // measured below: two wavefronts, MFMA only
 
 template <int CH, int RD, int NV>
@@ -170,6 +232,22 @@ double run(int waves_per_simd, long long* ticks, float* sink, const char* what, 
 }
 
 }  // namespace
+
+template <int RD, int GL, int PAT>
+void rung(long long* ticks, float* sink, const u32x4* gbuf, const char* what) {
+  double per = 0.0;
+  for (int rep = 0; rep < 3; ++rep) {
+    hipLaunchKernelGGL((mixg<RD, GL, PAT>), dim3(kBlocks), dim3(512), 0, 0, ticks, sink, gbuf);
+    if (hipDeviceSynchronize() != hipSuccess) return;
+    std::vector<long long> h(kBlocks * 8);
+    if (hipMemcpy(h.data(), ticks, h.size() * sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess) return;
+    double s = 0.0;
+    for (long long v : h) s += (double)v;
+    per = s / h.size() / kIters / 16.0;  // ticks per MFMA per wavefront
+  }
+  const double lds = RD * 1024.0 * 8 / (per * 16.0), glb = GL * 1024.0 * 8 / (per * 16.0);
+  printf("| %-58s | 2 | %6.1f | %5.1f %% | %6.1f | %6.1f |\n", what, per, 100.0 * kFullTicks * 2 / per, lds, glb);
+}
 
 // 16x16x32 loops at two wavefronts per SIMD, reported per 32 Kflop (one 32x32x16's work).
 template <int NA, int R, int NV>
@@ -210,5 +288,16 @@ int main() {
   run16<6, 3, 0>(ticks, sink, "R = 3 (1 KiB per 48 Kflop, 48 rows per wavefront)");
   run16<6, 3, 3>(ticks, sink, "R = 3, 3 VALU per 16x16x32 (6 per 32 Kflop)");
   run16<4, 4, 3>(ticks, sink, "R = 4 (1 KiB per 64 Kflop), 3 VALU per 16x16x32");
+  u32x4* gbuf = nullptr;
+  if (hipMalloc(&gbuf, 65536) != hipSuccess || hipMemset(gbuf, 0, 65536) != hipSuccess) return 1;
+  printf("\nOperands from global memory (L1/L2-resident 64 KiB) instead of LDS, 16 MFMAs per iteration:\n\n");
+  printf("| loop (per MFMA) | wavefronts per SIMD | ticks per MFMA per wavefront | MFMA pipe busy | LDS B/tick/CU | global B/tick/CU |\n");
+  printf("|---|---|---|---|---|---|\n");
+  rung<16, 0, 0>(ticks, sink, gbuf, "1 KiB LDS (reference)");
+  rung<8, 8, 0>(ticks, sink, gbuf, "512 B LDS + 512 B global, operand pattern");
+  rung<8, 8, 1>(ticks, sink, gbuf, "512 B LDS + 512 B global, whole rows");
+  rung<0, 16, 0>(ticks, sink, gbuf, "1 KiB global, operand pattern");
+  rung<0, 16, 1>(ticks, sink, gbuf, "1 KiB global, whole rows");
+  rung<0, 8, 1>(ticks, sink, gbuf, "512 B global, whole rows");
   return 0;
 }
