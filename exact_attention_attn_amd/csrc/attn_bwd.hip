@@ -183,38 +183,6 @@ struct TilePairDma {
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-
-// The 32 rows held by a wavefront's 32x32 accumulators (lane l: row l % 32; DB
-// accumulators of 32 columns each) -> bf16 rows [0, nrows) of a row-major tensor at dst0
-// (row stride in elements), through the wavefront's own LDS slice of 64 D bytes: written
-// in the accumulators' layout with the 16-byte chunk index XOR-swizzled by the row
-// (conflict-free), read back as whole rows, and stored 16 bytes per lane, so that each
-// store instruction writes 64 / (D / 8) complete rows instead of 16 bytes of 32 rows.
-template <int D>
-__device__ __forceinline__ void store_rows_lds(unsigned slice, uint16_t* dst0, int64_t stride, int nrows,
-                                               const f32x16* acc, float mul, int lane) {
-  constexpr int DB = D / 32, CPR = D / 8, RB = D * 2, RPI = 64 / CPR;
-  const int half = lane >> 5, row = lane & 31;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 r0 = (__bf16)(acc[db][4 * i + 0] * mul), r1 = (__bf16)(acc[db][4 * i + 1] * mul);
-      const __bf16 r2 = (__bf16)(acc[db][4 * i + 2] * mul), r3 = (__bf16)(acc[db][4 * i + 3] * mul);
-      const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
-      const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
-      const int c = 4 * db + i;  // chunk of columns 32 db + 8 i .. +7; this lane's half is 4 of them
-      *(lds_u32x2*)lds_at(slice + (unsigned)(row * RB + ((c ^ (row % CPR)) * 16) + 8 * half)) = u32x2{u0, u1};
-    }
-#pragma unroll
-  for (int n = 0; n < 32 / RPI; ++n) {
-    const int r = n * RPI + lane / CPR, c = lane % CPR;
-    const u32x4 v = *(const lds_u32x4*)lds_at(slice + (unsigned)(r * RB + ((c ^ (r % CPR)) * 16)));
-    if (r < nrows) *(u32x4*)(dst0 + (int64_t)r * stride + c * 8) = v;
-  }
-}
-
 // Variable-length launches in compact form: the batch's blocks of 128 rows (or keys),
 // sequence by sequence, are numbered without gaps; block u -> sequence s (-1 past the
 // last block), its block index blk and its row ranges [q0, q1) and [k0, k1) in the packed

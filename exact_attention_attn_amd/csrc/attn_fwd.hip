@@ -578,30 +578,19 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
       if (j < ntiles) step(j, kbuf1, kbuf0, vbuf0, vbuf1, sA, sB);
     }
 
-    // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2
-    if (qi < Lq) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      uint16_t* Og = (uint16_t*)p.o + ooff + (int64_t)qi * p.o_sn;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __bf16 r0 = (__bf16)(oacc[db][4 * i + 0] * inv);
-          __bf16 r1 = (__bf16)(oacc[db][4 * i + 1] * inv);
-          __bf16 r2 = (__bf16)(oacc[db][4 * i + 2] * inv);
-          __bf16 r3 = (__bf16)(oacc[db][4 * i + 3] * inv);
-          const unsigned u0 = (unsigned)__builtin_bit_cast(uint16_t, r0) | ((unsigned)__builtin_bit_cast(uint16_t, r1) << 16);
-          const unsigned u1 = (unsigned)__builtin_bit_cast(uint16_t, r2) | ((unsigned)__builtin_bit_cast(uint16_t, r3) << 16);
-          *(u32x2*)(Og + 32 * db + 8 * i + 4 * half) = u32x2{u0, u1};
-        }
-      if (p.lse != nullptr && half == 0)
-        p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
-    }
+    // ---- epilogue: O = O_acc / l, lse = (m2 + log2 l) * ln 2.  O goes through the
+    // wavefront's LDS slice (store_rows_lds): whole rows per store instruction.
+    __syncthreads();  // every wave is done with the K / V tiles
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    store_rows_lds<D>((unsigned)(uintptr_t)(const lds_void*)(smem + wave * 32 * D * 2),
+                      (uint16_t*)p.o + ooff + (int64_t)wrow0 * p.o_sn, p.o_sn, Lq - wrow0, oacc, inv, lane);
+    if (qi < Lq && p.lse != nullptr && half == 0)
+      p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
   };  // row_block
 
   row_block(rbs[0]);
   if (rbs[1] != rbs[0]) {
-    __syncthreads();  // every wave is done with the first block's LDS tiles
+    __syncthreads();  // every wave is done with the first block's LDS (its O slices)
     row_block(rbs[1]);
   }
 }
