@@ -497,7 +497,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // which every wave finished before reaching that barrier.  Five stages.
   // (a barrier every third or fourth step, with rings of 7 or 9 stages, measured slower)
   constexpr int STAGES = 5;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF];
+  // after the ring: each wavefront's K and V rows, staged on their way into registers
+  // (one workgroup per CU, so the LDS this adds costs no occupancy)
+  constexpr int KV_STAGE = 2 * TILE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * BUF + NW * KV_STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -551,19 +554,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* K = (const uint16_t*)p.k + geo.k0;
   const uint16_t* V = (const uint16_t*)p.v + geo.k0;
 
-  // keys past the end load the last key (no divergent branch around the loads) and are
-  // zeroed; their dK / dV are never stored
-  const bool kin = key < Lk;
-  const int64_t krow = min(key, Lk - 1);
-  bf16x8 kreg[DT], vreg[DT];
+  // This wavefront's 32 K rows and 32 V rows come through LDS: direct-to-LDS loads of
+  // whole rows (1 KiB blocks) into its staging slot, in the swizzled tile layout that
+  // op_read reads as the B operands (one key per lane).  Loads straight into the operand
+  // layout would make each load instruction touch 32 rows for 32 bytes each; this way
+  // the registers are filled about 2.5 us sooner after the workgroup starts.  Keys past
+  // the end load the last key (their P and dS are masked to zero, their dK / dV never
+  // stored).
+  const unsigned kv_slot = lds_addr(smem) + (unsigned)(STAGES * BUF + wave * KV_STAGE);
+  {
+    const int wk0 = k0 + wave * 32;
+    const int last = max(0, min(31, Lk - 1 - wk0));  // last valid row of this wavefront's keys
+    const u32x4s kr = biased_rsrc(K + (int64_t)min(wk0, Lk - 1) * geo.krs);
+    const u32x4s vr = biased_rsrc(V + (int64_t)min(wk0, Lk - 1) * geo.krs);
+    constexpr int NBT = TILE / 1024;  // 1 KiB blocks per tensor
+    static_assert(NBT % 4 == 0, "whole groups of four blocks");
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 a = *(const u32x4*)(K + krow * geo.krs + 16 * t + 8 * half);
-    const u32x4 c = *(const u32x4*)(V + krow * geo.krs + 16 * t + 8 * half);
-    kreg[t] = as_bf16x8(kin ? a : z);
-    vreg[t] = as_bf16x8(kin ? c : z);
+    for (int g = 0; g < NBT / 4; ++g) {
+      int vo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 2 * (4 * g + i) + (lane >> 5);
+        const int row = min((lane & 31) ^ (4 * (c & 3)), last);
+        vo[i] = row * (geo.krs * 2) + c * 16 - i * 1024 + kDmaBias;
+      }
+      dma4(kr, kv_slot + (unsigned)(g * 4096), vo[0], vo[1], vo[2], vo[3]);
+      dma4(vr, kv_slot + (unsigned)(TILE + g * 4096), vo[0], vo[1], vo[2], vo[3]);
+    }
   }
+  bf16x8 kreg[DT], vreg[DT];  // filled from the staging slot once the loads landed
   const float c2 = p.scale_log2;
 
   // query tiles of one head that can see any key of this block
@@ -754,12 +773,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int st = 0; st < 3; ++st)
     if (st < nsteps) issue();
-  // the K / V register loads are waited for here, after the first tiles' loads are issued
-  settle(kreg);
-  settle(vreg);
+  wait_vm<0>();  // this wave's K / V rows (and its share of the first tiles) landed
+  {
+    const unsigned o0 = opaque(kv_slot + sw_op_lane(lane, 0)), o1 = opaque(kv_slot + sw_op_lane(lane, 1));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      kreg[t] = op_read((t & 1) ? o1 : o0, t);
+      vreg[t] = op_read(((t & 1) ? o1 : o0) + TILE, t);
+    }
+  }
   f32x16 sA, dA, sB, dB;
   if (nsteps > 0) {
-    wait_vm<0>();
     __syncthreads();
     products(sA, dA);
   }
