@@ -555,6 +555,57 @@ def test_backward_row_sum_identity():
     assert np.abs((p * (do @ v.T)).sum(axis=1) - (do * o).sum(axis=1)).max() < TIGHT
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_given_exact_o_matches_default(causal):
+    """Handed the exact forward output, the backward forms D_i = dO_i . O_i from it and
+    gets the same gradients as from P and dP (rows without keys included)."""
+    r = rng(76)
+    q, do = r.normal(size=(7, 4)), r.normal(size=(7, 3))
+    k, v = r.normal(size=(5, 4)), r.normal(size=(5, 3))
+    o, _ = oracle.attention_rows(q, k, v, 0.6, causal)
+    a = oracle.attention_backward_rows(q, k, v, do, 0.6, causal)
+    b = oracle.attention_backward_rows(q, k, v, do, 0.6, causal, o=o)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() < TIGHT
+
+
+def test_backward_given_o_shifts_only_the_row_sum():
+    """A perturbed O moves D_i by dO_i . delta_i and nothing else: dQ_i shifts by
+    -scale (dO_i . delta_i) sum_j P_ij K_j, dK_j by -scale sum_i P_ij (dO_i . delta_i) Q_i,
+    and dV does not move (closed forms from dS = P (dP - D))."""
+    r = rng(77)
+    q, do = r.normal(size=(6, 4)), r.normal(size=(6, 3))
+    k, v = r.normal(size=(6, 4)), r.normal(size=(6, 3))
+    scale = 0.7
+    o, _ = oracle.attention_rows(q, k, v, scale, True)
+    delta = 1e-3 * r.normal(size=o.shape)
+    dq0, dk0, dv0 = oracle.attention_backward_rows(q, k, v, do, scale, True, o=o)
+    dq1, dk1, dv1 = oracle.attention_backward_rows(q, k, v, do, scale, True, o=o + delta)
+    p = oracle.probabilities(q, k, scale, True)
+    dd = (do * delta).sum(axis=1)                      # shift of D_i
+    assert np.abs((dq1 - dq0) - (-scale * dd[:, None] * (p @ k))).max() < TIGHT
+    assert np.abs((dk1 - dk0) - (-scale * (p * dd[:, None]).T @ q)).max() < TIGHT
+    assert np.abs(dv1 - dv0).max() == 0.0
+
+
+def test_backward_given_o_dense_and_varlen_pass_it_per_head():
+    """The dense and varlen entries hand each head its own rows of O."""
+    r = rng(78)
+    q, do = r.normal(size=(1, 4, 5, 3)), r.normal(size=(1, 4, 5, 3))
+    k, v = r.normal(size=(1, 2, 5, 3)), r.normal(size=(1, 2, 5, 3))
+    o = r.normal(size=(1, 4, 5, 3))
+    got = oracle.attention_backward_dense(q, k, v, do, 0.5, True, o=o)
+    for h in range(4):
+        hk = h // 2
+        want = oracle.attention_backward_rows(q[0, h], k[0, hk], v[0, hk], do[0, h], 0.5, True, o=o[0, h])
+        assert np.abs(got[0][0, h] - want[0]).max() < TIGHT
+    t = lambda x: x[0].transpose(1, 0, 2)  # [1, H, N, d] -> [N, H, d]
+    cu = np.array([0, 5])
+    gv = oracle.attention_backward_varlen(t(q), t(k), t(v), t(do), cu, cu, 0.5, True, o=t(o))
+    assert np.abs(gv[0] - t(got[0])).max() < TIGHT
+    assert np.abs(gv[1] - t(got[1])).max() < TIGHT
+
+
 def test_backward_gqa_sums_group_gradients():
     """A KV head's gradient is the sum over the query heads reading it: equal to the
     gradient of the explicitly expanded K/V summed back over the copies."""
