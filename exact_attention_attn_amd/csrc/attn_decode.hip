@@ -427,7 +427,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-// One wavefront per (sequence, head); lane owns D/64 columns.
+// One wavefront per (sequence, head); lane owns D/64 columns.  The splits' (m, l) are read
+// one split per lane (64 at a time) and reduced across the wavefront; each split's weight
+// 2^(m_c - M) is then broadcast from its lane while the lanes add up their columns of the
+// partial outputs in split order, with those loads issued eight splits at a time, so the
+// combine costs a few memory round trips instead of one per split.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams p) {
   constexpr int CPL = D / 64;
@@ -440,19 +444,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams 
   const int64_t base = (int64_t)bh * p.max_splits;
 
   float M = kNegInf;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, p.ws_ml[(base + c) * 2]);
+  for (int c0 = 0; c0 < ns; c0 += 64)
+    if (c0 + lane < ns) M = fmaxf(M, p.ws_ml[(base + c0 + lane) * 2]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
   const float Mu = (M == kNegInf) ? 0.f : M;
   float L = 0.f, o[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) o[e] = 0.f;
-  for (int c = 0; c < ns; ++c) {
-    const float2 ml = *(const float2*)(p.ws_ml + (base + c) * 2);
-    const float w = exp2_fast(ml.x - Mu);
-    L = __builtin_fmaf(w, ml.y, L);
-    const float* a = p.ws_acc + (base + c) * D + lane * CPL;
+  for (int c0 = 0; c0 < ns; c0 += 64) {
+    // this chunk's weights and row sums, one split per lane
+    float w = 0.f, lw = 0.f;
+    if (c0 + lane < ns) {
+      const float2 ml = *(const float2*)(p.ws_ml + (base + c0 + lane) * 2);
+      w = exp2_fast(ml.x - Mu);
+      lw = w * ml.y;
+    }
+    L += lw;
+    const int n = min(64, ns - c0);
+    for (int c = 0; c < n; c += 8) {
+      float a[8][CPL];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) o[e] = __builtin_fmaf(w, a[e], o[e]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+          a[u][e] = c + u < n ? p.ws_acc[(base + c0 + c + u) * D + lane * CPL + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(c + u, 63)));
+        if (c + u < n) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) o[e] = __builtin_fmaf(wu, a[u][e], o[e]);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d);
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   uint16_t* O = (uint16_t*)p.o + (int64_t)bh * D + lane * CPL;
 #pragma unroll
