@@ -335,6 +335,24 @@ def test_decode_long_context(A, H, H_kv):
     assert_close("lse", lse, rl, TOL_BF16_LSE)
 
 
+@pytest.mark.parametrize("H,H_kv,d", [(4, 4, 64), (8, 2, 128)])
+def test_decode_split_counts_at_combine_boundaries(A, H, H_kv, d):
+    """The combine reads the splits' (m, l) one split per lane in chunks of 64 and the
+    partial outputs eight splits at a time: 512-token splits counts of 8, 9, 64 and 65
+    (and one single-token context) put a sequence on each of those boundaries."""
+    import torch
+    ctx = [4096, 4097, 32768, 32769, 1]
+    w = synth.paged(H=H, d=d, ctx=ctx, page=16, seed=97, H_kv=H_kv)
+    o, lse = A.attn_decode_paged(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                                 dev(w.context_lens), max(ctx), scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attention_decode_paged(w.q, w.k_cache, w.v_cache, w.block_table, w.context_lens, w.scale)
+    assert_close("O", o, ro, TOL_BF16_O)
+    assert_close("lse", lse, rl, TOL_BF16_LSE)
+
+
 def test_decode_context_above_max_is_truncated(A):
     """A context length above max_context_len (a caller error) is truncated to
     max_context_len, in the split kernels and in the combine.  The block table and the
