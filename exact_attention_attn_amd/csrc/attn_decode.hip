@@ -20,9 +20,10 @@
 //    of matrix-core tiles, so each K/V row is read once for the whole group and the
 //    per-head cost is absorbed by the MFMA.
 // The combine kernel merges the splits of each (sequence, head): with M = max_c m_c,
-// O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, lse = (M + log2 L) ln 2, in split
-// order (deterministic).  This is the online-softmax rescale applied to partial
-// states ("L2.5 SOTA Kernel", yulong.wang, section 2.2).
+// O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, lse = (M + log2 L) ln 2; the O
+// sums run in split order and L by a fixed reduction tree (deterministic).  This is the
+// online-softmax rescale applied to partial states ("L2.5 SOTA Kernel", yulong.wang,
+// section 2.2).
 #include "attn_internal.h"
 #include "attn_tile.h"
 
