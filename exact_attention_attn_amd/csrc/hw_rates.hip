@@ -1,8 +1,10 @@
 // Hardware rates behind the forward kernel's roofline on gfx950: how fast one SIMD
 // issues 32x32x16 bf16 MFMAs alone, next to VALU work, and next to LDS operand reads of
 // the two sizes a wavefront tile can have (1 KiB per MFMA with 32 query rows per
-// wavefront, 512 B with 64); and the same for 16x16x32 MFMAs whose LDS operand serves 2-4
-// query blocks of 16 rows.  A measurement aid, not part of libattn.so.
+// wavefront, 512 B with 64); the same for 16x16x32 MFMAs whose LDS operand serves 2-4
+// query blocks of 16 rows; operands from global memory; and a forward split by role (one
+// wavefront computes S and P for 64 rows, its partner accumulates O).  A measurement aid,
+// not part of libattn.so.
 //
 // Each test runs one workgroup per CU (the LDS array is sized above half of a CU's LDS)
 // of 4 or 8 wavefronts, i.e. 1 or 2 wavefronts per SIMD, and times its loop with the
@@ -201,6 +203,93 @@ __global__ void __launch_bounds__(512) mixg(long long* ticks, float* sink, const
   if (lane == 0) ticks[blockIdx.x * 8 + wave] = t1 - t0;
 }
 
+// A forward split by role, two wavefronts per SIMD (8 per workgroup; wavefronts w and
+// w + 4 share a SIMD, which the test reads back from HW_ID): wavefronts 0-3 play "S"
+// (16 MFMAs per tile whose 1 KiB LDS operand serves two 32-row query blocks: RDS reads;
+// NVS VALU instructions per MFMA, the whole softmax of 64 rows; WRS 16-byte LDS writes
+// per lane, P for the partner) and wavefronts 4-7 play "PV" (16 MFMAs, RDP reads: the
+// V^T operands shared by two query blocks and the partner's P; NVP VALU per MFMA).
+// BAR: a workgroup barrier per tile, as the hand-over of P needs.  The same template
+// with equal roles is the present kernel's mix.
+template <int RDS, int NVS, int WRS, int RDP, int NVP, bool BAR>
+__global__ void __launch_bounds__(512) mixrole(long long* ticks, unsigned* simd, float* sink, float a, float b) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid * 16; i < 65536; i += blockDim.x * 16) *(u32x4*)(sm + i) = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  const bool S = wave < 4;
+  const int RD = S ? RDS : RDP;
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = f32x16{};
+  bf16x8 A, B;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    A[i] = (__bf16)(0.5f + i * 0.01f);
+    B[i] = (__bf16)(0.25f - i * 0.01f);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = a + 0.01f * lane + 0.1f * i;
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)sm;
+  const unsigned off = (unsigned)(wave * 4096 + lane * 16);
+  // P slots: 2 KiB per wavefront from byte 65536 on (the last ends at 81920)
+  const unsigned woff = 65536u + (unsigned)(wave * 2048 + lane * 16);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const long long t0 = clock64();
+  for (int it = 0; it < kIters; ++it) {
+    u32x4 r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < RD) r[i] = *(const lds_u32x4*)(base + ((off + ((it * 7 + i) & 15) * 1024) & 0xFFF0u));
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      c[m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, c[m % 4], 0, 0, 0);
+      if (S) {
+#pragma unroll
+        for (int v = 0; v < NVS; ++v) {
+          const int i = (m * NVS + v) & 7;
+          if (v % 3 == 1) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+          else x[i] = __builtin_fmaf(x[i], a, b);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < NVP; ++v) {
+          const int i = (m * NVP + v) & 7;
+          if (v % 3 == 1) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+          else x[i] = __builtin_fmaf(x[i], a, b);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < RD) acc ^= r[i];
+    if (S) {
+#pragma unroll
+      for (int w = 0; w < WRS; ++w)
+        *(lds_u32x4*)(base + woff + (unsigned)((w & 1) * 1024)) = u32x4{__builtin_bit_cast(unsigned, x[w & 7]), acc.x, 0u, 0u};
+    }
+    if (BAR) __syncthreads();
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const long long t1 = clock64();
+  float s = (float)(acc.x + acc.y + acc.z + acc.w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  if (s == 1234.5f) sink[tid] = s;  // keeps the work; never true
+  if (lane == 0) {
+    unsigned hw;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    ticks[blockIdx.x * 8 + wave] = t1 - t0;
+    simd[blockIdx.x * 8 + wave] = (hw >> 4) & 3u;  // SIMD_ID
+  }
+}
+
 constexpr double kFullTicks = 24.0;  // measured below: two wavefronts, MFMA only
 
 template <int CH, int RD, int NV>
@@ -266,6 +355,33 @@ void run16(long long* ticks, float* sink, const char* what) {
   printf("| %-58s | 2 | %6.1f | %5.1f %% | %6.1f |\n", what, per, 100.0 * kFullTicks * 2 / per, lds);
 }
 
+// Role-split loops: ticks per MFMA of the slowest wavefront (the tile loop's pace when
+// the roles are coupled), and in how many workgroups wavefronts w and w + 4 shared a SIMD.
+template <int RDS, int NVS, int WRS, int RDP, int NVP, bool BAR>
+void runrole(long long* ticks, unsigned* simd, float* sink, const char* what) {
+  double per = 0.0;
+  int shared = 0;
+  for (int rep = 0; rep < 3; ++rep) {
+    hipLaunchKernelGGL((mixrole<RDS, NVS, WRS, RDP, NVP, BAR>), dim3(kBlocks), dim3(512), 0, 0, ticks, simd, sink,
+                       0.3f, 0.7f);
+    if (hipDeviceSynchronize() != hipSuccess) return;
+    std::vector<long long> h(kBlocks * 8);
+    std::vector<unsigned> sd(kBlocks * 8);
+    if (hipMemcpy(h.data(), ticks, h.size() * sizeof(long long), hipMemcpyDeviceToHost) != hipSuccess) return;
+    if (hipMemcpy(sd.data(), simd, sd.size() * sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess) return;
+    long long mx = 0;
+    for (long long v : h) mx = v > mx ? v : mx;
+    per = (double)mx / kIters / 16.0;
+    shared = 0;
+    for (int b = 0; b < kBlocks; ++b) {
+      bool ok = true;
+      for (int w = 0; w < 4; ++w) ok = ok && sd[b * 8 + w] == sd[b * 8 + w + 4];
+      shared += ok ? 1 : 0;
+    }
+  }
+  printf("| %-58s | 2 | %6.1f | %5.1f %% | %d / %d |\n", what, per, 100.0 * kFullTicks * 2 / per, shared, kBlocks);
+}
+
 int main() {
   long long* ticks = nullptr;
   float* sink = nullptr;
@@ -299,5 +415,16 @@ int main() {
   rung<0, 16, 0>(ticks, sink, gbuf, "1 KiB global, operand pattern");
   rung<0, 16, 1>(ticks, sink, gbuf, "1 KiB global, whole rows");
   rung<0, 8, 1>(ticks, sink, gbuf, "512 B global, whole rows");
+  unsigned* simd = nullptr;
+  if (hipMalloc(&simd, kBlocks * 8 * sizeof(unsigned)) != hipSuccess) return 1;
+  printf("\nA forward split by role (per SIMD one S and one PV wavefront, 16 MFMAs each per tile), against the\n"
+         "present mix (every wavefront: 16 MFMAs, 16 KiB of LDS reads, 5 VALU per MFMA); slowest wavefront:\n\n");
+  printf("| loop per tile | wavefronts per SIMD | ticks per MFMA | MFMA pipe busy | workgroups with w, w + 4 on one SIMD |\n");
+  printf("|---|---|---|---|---|\n");
+  runrole<16, 5, 0, 16, 5, false>(ticks, simd, sink, "present mix");
+  runrole<16, 5, 0, 16, 5, true>(ticks, simd, sink, "present mix, barrier per tile");
+  runrole<8, 10, 4, 12, 0, true>(ticks, simd, sink, "split: S 8 KiB + 10 VALU/MFMA + P, PV 12 KiB; barrier");
+  runrole<8, 10, 4, 12, 0, false>(ticks, simd, sink, "split as above, no barrier");
+  runrole<8, 0, 0, 12, 0, true>(ticks, simd, sink, "split without the softmax VALU; barrier");
   return 0;
 }
