@@ -596,26 +596,37 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 }
 
 // ----------------------------------------------------------------------------------
-// fp32 VALU kernel (dense only): 64 query rows per workgroup, 4 lanes per row.
+// fp32 VALU kernel (dense only): kFwdF32BM = 16 query rows per workgroup, 4 lanes per row
+// in each of its NWV wavefronts (8 at d = 64, 4 at d = 128: one K / V slot each in LDS).
+// The wavefronts take the key tiles in turn (tile j to wavefront j mod NWV), each
+// through its own slot with no barrier in the loop, so a row block's keys are walked NWV
+// tiles at a time; the partial states (m, l, O) merge through LDS at the end, as the
+// decode combine merges splits.
 // ----------------------------------------------------------------------------------
+template <int D>
+constexpr int f32_waves() { return D == 64 ? 8 : 4; }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * f32_waves<D>()) void fwd_f32_kernel(const FwdParams p) {
   constexpr int DL = D / 4;   // columns per lane
   constexpr int KT = 32;      // keys per LDS tile
   constexpr int RS = D + 4;   // LDS row stride (floats)
-  __shared__ __attribute__((aligned(16))) float Ksh[KT * RS];
-  __shared__ __attribute__((aligned(16))) float Vsh[KT * RS];
+  constexpr int NWV = f32_waves<D>();  // wavefronts, each with its own K / V slot
+  constexpr int SLOT = 2 * KT * RS;
+  constexpr int PS = D + 2;   // merge record of a row: O, m, l
+  static_assert(kFwdF32BM * PS <= SLOT, "a wavefront's merge records fit its slot");
+  __shared__ __attribute__((aligned(16))) float sm[NWV * SLOT];
 
-  const int tid = threadIdx.x;
-  const int row = tid >> 2;
-  const int part = tid & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane >> 2;
+  const int part = lane & 3;
   int rb, b, h;
   block_coords<CAUSAL>(p, rb, b, h);
   int Lq, Lk;
   int64_t qoff, koff, voff, ooff, loff;
   seq_bounds<false>(p, b, h, Lq, Lk, qoff, koff, voff, ooff, loff);
   const int row0 = rb * kFwdF32BM;
-  if (row0 >= Lq) return;
+  if (row0 >= Lq) return;  // uniform over the workgroup
   const int shift = Lk - Lq;
   int kend = Lk;
   if (CAUSAL) kend = min(Lk, max(0, row0 + kFwdF32BM + shift));
@@ -634,11 +645,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
   }
   float m2 = kNegInf, l = 0.f;
   const float c2 = p.scale_log2;
+  float* const Ksh = sm + wave * SLOT;
+  float* const Vsh = Ksh + KT * RS;
 
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = wave; j < ntiles; j += NWV) {
     const int kt0 = j * KT;
-    __syncthreads();
-    for (int idx = tid; idx < KT * (D / 4); idx += 256) {
+    // The slot's reads of the previous tile precede these writes in this wavefront's
+    // program, and LDS instructions of one wavefront complete in order.
+    asm volatile("" ::: "memory");
+    for (int idx = lane; idx < KT * (D / 4); idx += 64) {
       const int key = idx / (D / 4), c4 = idx % (D / 4);
       const int gk = kt0 + key;
       float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
@@ -649,7 +664,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
       *(float4*)(Ksh + key * RS + 4 * c4) = kv;
       *(float4*)(Vsh + key * RS + 4 * c4) = vv;
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");
 
     float s[KT];
     float mx = kNegInf;
@@ -677,22 +692,50 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdParams p) {
     l = l * alpha + rs;
     m2 = mnew;
 #pragma unroll
-    for (int c = 0; c < DL; ++c) {
-      float acc = o[c] * alpha;
+    for (int c = 0; c < DL; ++c) o[c] *= alpha;
+    // key by key, so that one key's V values are live at a time
 #pragma unroll
-      for (int jj = 0; jj < KT; ++jj) acc = __builtin_fmaf(s[jj], Vsh[jj * RS + part * DL + c], acc);
-      o[c] = acc;
+    for (int jj = 0; jj < KT; ++jj) {
+      const float* vr = Vsh + jj * RS + part * DL;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) o[c] = __builtin_fmaf(s[jj], vr[c], o[c]);
     }
   }
 
-  if (qi < Lq) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    float* Og = (float*)p.o + ooff + (int64_t)qi * p.o_sn + part * DL;
+  // Merge: each wavefront's (O, m, l) per row into its slot; wavefront 0 combines them,
+  // M = max_w m_w, O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w, in wavefront order.
+  __syncthreads();  // every wavefront is done with its tiles
+  {
+    float* rec = sm + wave * SLOT + row * PS;
 #pragma unroll
-    for (int c = 0; c < DL; ++c) Og[c] = o[c] * inv;
-    if (p.lse != nullptr && part == 0)
-      p.lse[loff + (int64_t)qi * p.l_sn] = l > 0.f ? (m2 + log2f(l)) * kLn2 : kNegInf;
+    for (int c = 0; c < DL; ++c) rec[part * DL + c] = o[c];
+    if (part == 0) {
+      rec[D] = m2;
+      rec[D + 1] = l;
+    }
   }
+  __syncthreads();
+  if (wave != 0 || qi >= Lq) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm[w * SLOT + row * PS + D]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, acc[DL];
+#pragma unroll
+  for (int c = 0; c < DL; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const float* rec = sm + w * SLOT + row * PS;
+    const float wt = exp2f(rec[D] - Mu);  // 0 for a wavefront that saw no admissible key
+    L = __builtin_fmaf(wt, rec[D + 1], L);
+#pragma unroll
+    for (int c = 0; c < DL; ++c) acc[c] = __builtin_fmaf(wt, rec[part * DL + c], acc[c]);
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  float* Og = (float*)p.o + ooff + (int64_t)qi * p.o_sn + part * DL;
+#pragma unroll
+  for (int c = 0; c < DL; ++c) Og[c] = acc[c] * inv;
+  if (p.lse != nullptr && part == 0) p.lse[loff + (int64_t)qi * p.l_sn] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -732,7 +775,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_f32_t(const FwdParams& p, hipStream_t s) {
   const int64_t nblk = (int64_t)p.n_rb * p.H * p.B;
   if (nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(64 * f32_waves<D>()), 0, s, p);
   return hipGetLastError();
 }
 

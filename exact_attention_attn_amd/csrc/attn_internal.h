@@ -126,8 +126,8 @@ constexpr int kFwdShortBN = 32, kFwdShortWPE = 3;
 constexpr int kFwdShortLen = 4096;
 // Row-block height of the bf16 forward kernel (query rows per workgroup).
 constexpr int kFwdBM = 32 * kFwdNW;
-// Row-block height of the fp32 forward kernel.
-constexpr int kFwdF32BM = 64;
+// Row-block height of the fp32 forward kernel (its four wavefronts split the keys).
+constexpr int kFwdF32BM = 16;
 // Tokens per decode split (a multiple of 16).
 #ifndef ATTN_DECODE_SPLIT
 #define ATTN_DECODE_SPLIT 512

@@ -179,7 +179,9 @@ def test_dense_ragged_bf16(A, N, Nk, causal, d):
 
 
 @pytest.mark.parametrize("N,Nk,causal,d", [(1, 1, False, 64), (100, 100, True, 64), (130, 70, True, 128),
-                                           (70, 130, True, 128), (257, 257, False, 128)])
+                                           (70, 130, True, 128), (257, 257, False, 128),
+                                           # several key tiles per wavefront of the fp32 kernel
+                                           (300, 1100, True, 64), (1000, 1000, False, 64)])
 def test_dense_ragged_fp32(A, N, Nk, causal, d):
     w = synth.dense(2, 2, N, d, "f32", causal, seed=N + 3 * Nk, Nk=Nk)
     o, lse = run_dense(A, w)
