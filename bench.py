@@ -50,8 +50,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 # (FETCH_SIZE reads half of the bytes moved: x2; WRITE_SIZE x1), per workload.  Valid
 # only for the kernel source they were taken on (sha256 prefix of attn_fwd.hip followed
 # by the attn_tile.h and attn_internal.h it includes); reported as null otherwise.
-FWD_COUNTERS = {"source_sha256_16": "74ce2604c4792147", "fetch_scale": 2.0, "write_scale": 1.0,
-                "c3": {"fetch_kib": 130982.75, "write_kib": 66560.0},
+FWD_COUNTERS = {"source_sha256_16": "7d972f05332f4deb", "fetch_scale": 2.0, "write_scale": 1.0,
+                "c3": {"fetch_kib": 130930.9375, "write_kib": 66560.0},
                 "c2": {"fetch_kib": 49280.5, "write_kib": 33280.0}}
 
 
