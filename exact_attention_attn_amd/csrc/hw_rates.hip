@@ -94,8 +94,9 @@ __device__ __forceinline__ void fill_lds(unsigned char* sm) {
 // TLV (tile-load variant, direct-to-LDS only): 0 as the forward (s_nop 4 after the M0 write,
 // all blocks issued after the barrier, waited for before the next); 1 s_nop 0; 2 one block
 // issued after every fourth MFMA instead; 3 no wait before the barrier (timing only).
+// BE: tiles per barrier (2: the loads of two tiles issued after each barrier, a four-stage ring).
 template <int MODE, int CH, int NF, int NE, bool BAR, int LDSB = kLdsBytes, int TL = 0, int NB = 8, bool SH = false,
-          int TLV = 0>
+          int TLV = 0, int BE = 1>
 __global__ void __launch_bounds__(512) tile_loop(long long* ticks, float* sink, float a, float b,
                                                  const unsigned char* gbuf) {
   __shared__ __attribute__((aligned(1024))) unsigned char sm[LDSB];
@@ -212,10 +213,12 @@ __global__ void __launch_bounds__(512) tile_loop(long long* ticks, float* sink, 
         if (m % 4 == 0 && m / 4 < NB) issue_block(t, m / 4);
       }
       if (m == 15 || m == 31) {
-        if (m == barpos) {  // uniform per wavefront; every wavefront meets one barrier per tile
+        if (m == barpos && t % BE == BE - 1) {  // uniform per wavefront; every wavefront meets the same barriers
           land_tile();
           if (BAR) __syncthreads();
-          if constexpr (TL != 0) issue_tile(t + 1);
+          if constexpr (TL != 0)
+#pragma unroll
+            for (int u = 1; u <= BE; ++u) issue_tile(t + u);
         }
       }
     }
@@ -332,10 +335,10 @@ double mean_ticks(K kernel, int threads, long long* ticks, float* sink, int bloc
 // workgroups of 4 wavefronts per CU, whose wavefronts pair up on the SIMDs as in the
 // forward kernel.
 template <int MODE, int CH, int NF, int NE, bool BAR, bool TWO_WG = false, int TL = 0, int NB = 8, bool SH = false,
-          int TLV = 0>
+          int TLV = 0, int BE = 1>
 void run(int wps, long long* ticks, float* sink, const char* what) {
-  const double t = TWO_WG ? mean_ticks(tile_loop<MODE, CH, NF, NE, BAR, 65536, TL, NB, false, TLV>, 256, ticks, sink, 2 * kBlocks)
-                          : mean_ticks(tile_loop<MODE, CH, NF, NE, BAR, kLdsBytes, TL, NB, SH>, 256 * wps, ticks, sink);
+  const double t = TWO_WG ? mean_ticks(tile_loop<MODE, CH, NF, NE, BAR, 65536, TL, NB, false, TLV, BE>, 256, ticks, sink, 2 * kBlocks)
+                          : mean_ticks(tile_loop<MODE, CH, NF, NE, BAR, kLdsBytes, TL, NB, SH, 0, BE>, 256 * wps, ticks, sink);
   if (t < 0) return;
   const double per = t / (kTiles * 32.0);  // ticks per MFMA per wavefront
   if (g_full == 0.0) g_full = per / wps;
@@ -404,6 +407,8 @@ int main() {
   run<3, 4, 4, 1, true, false, 1, 4>(2, ticks, sink, "8 wavefronts (256 rows), barrier, 4 KiB direct-to-LDS");
   run<3, 4, 4, 1, true, false, 1, 4, true>(2, ticks, sink, "the same, wavefronts 4-7 half a tile behind");
   run<3, 4, 4, 1, false, false, 1, 4>(2, ticks, sink, "8 wavefronts, 4 KiB direct-to-LDS, no barrier");
+  run<3, 4, 4, 1, true, false, 1, 4, false, 0, 2>(2, ticks, sink, "8 wavefronts, 4 KiB direct-to-LDS, barrier every 2nd tile");
+  run<3, 4, 4, 1, true, true, 1, 8, false, 0, 2>(2, ticks, sink, "two workgroups of 4, 8 KiB, barrier every 2nd tile");
   run<4, 4, 4, 1, false>(2, ticks, sink, "512 B operand per MFMA (64 rows per wavefront) + 5 VALU");
   run<0, 8, 4, 1, false>(1, ticks, sink, "no LDS, 5 VALU, 8 chains");
   run<4, 8, 4, 1, false>(1, ticks, sink, "512 B per MFMA + 5 VALU, 8 chains (64 rows per wavefront)");
