@@ -52,7 +52,7 @@ __device__ __forceinline__ unsigned opaque(unsigned a) {
   asm volatile("" : "+v"(a));
   return a;
 }
-__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
+__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
 
 // Swizzled [32 rows, D] bf16 tile serving both read patterns without bank conflicts:
 // 16-byte chunk c (columns 8 c .. 8 c + 7) of row r sits at c * 512 + (r ^ 4 (c % 4)) * 16.

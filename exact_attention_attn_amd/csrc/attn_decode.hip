@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
 }
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)a; }
+__device__ __forceinline__ const lds_u8* lds_at(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
 
 // Grouped-query decode on the matrix cores (the per-head VALU work of
 // decode_split_kernel grows with the group): one wavefront per (sequence, split,
